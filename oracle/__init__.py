@@ -1,0 +1,235 @@
+"""CPU oracle for ReplaySSM prefix materialize -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It marshals numpy arrays into the plain C oracle
+(``rssm_oracle.c``); every step of the arithmetic is there.  It imports
+nothing from the HIP path; inputs come from ``rssm_inputs``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import List, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librssm_oracle.so")
+SRC_PATH = os.path.join(_HERE, "rssm_oracle.c")
+
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3, "f8e4m3": 4, "f64": 5}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "f8e4m3": 1, "f64": 8}
+STORAGE_NP = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16,
+              "i8": np.int8, "f8e4m3": np.uint8, "f64": np.float64}
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_layers", "batch", "num_heads", "heads_per_group", "dim", "dstate", "max_window",
+        "ring_len", "pad_slot_id", "philox_rounds", "state_dtype", "input_dtype")] + [
+        ("seed", ctypes.c_uint64)]
+
+
+_VP = ctypes.c_void_p
+_P = ctypes.POINTER
+
+
+class _Inputs(ctypes.Structure):
+    _fields_ = [("state", _P(_VP)), ("state_stride", _P(ctypes.c_int64)),
+                ("scale", _P(_VP)), ("scale_stride", _P(ctypes.c_int64)),
+                ("x", _P(_VP)), ("x_stride", _P(ctypes.c_int64)),
+                ("Bm", _P(_VP)), ("B_stride", _P(ctypes.c_int64)),
+                ("dt", _P(_VP)), ("dt_stride", _P(ctypes.c_int64)),
+                ("A", _P(_VP)),
+                ("src_slots", _P(ctypes.c_int32)), ("dst_slots", _P(ctypes.c_int32)),
+                ("ring_start", _P(ctypes.c_int32)), ("prefix_len", _P(ctypes.c_int32)),
+                ("active", _P(ctypes.c_int32))]
+
+
+class _Outputs(ctypes.Structure):
+    _fields_ = [("state", _P(_VP)), ("scale", _P(_VP)), ("exact", _P(_VP)), ("mag", _P(_VP))]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        L.orc_materialize.argtypes = [_P(_Params), _P(_Inputs), _P(_Outputs)]
+        L.orc_materialize.restype = ctypes.c_int
+        L.orc_tile.argtypes = [_P(_Params), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                               _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.orc_tile.restype = ctypes.c_int
+        L.orc_encode_row.argtypes = [_P(_Params), _VP, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, _VP, _VP]
+        L.orc_encode_row.restype = ctypes.c_int
+        L.orc_round_value.argtypes = [ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_uint32]
+        L.orc_round_value.restype = ctypes.c_uint32
+        L.orc_decode.argtypes = [ctypes.c_int32, _VP, ctypes.c_int64]
+        L.orc_decode.restype = ctypes.c_double
+        L.orc_philox4x32.argtypes = [_P(ctypes.c_uint32), _P(ctypes.c_uint32), ctypes.c_int32,
+                                     _P(ctypes.c_uint32)]
+        L.orc_philox4x32.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle buffers must be C-contiguous"
+    return a.ctypes.data_as(_VP)
+
+
+def _ptr_array(arrs):
+    return (_VP * len(arrs))(*[a.ctypes.data for a in arrs])
+
+
+def _i64(vals):
+    return (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+
+
+def _i32p(a: np.ndarray):
+    return np.ascontiguousarray(a, np.int32).ctypes.data_as(_P(ctypes.c_int32))
+
+
+def params(spec, state_dtype: Optional[str] = None, philox_rounds: Optional[int] = None,
+           seed: Optional[int] = None) -> _Params:
+    rounds = spec.philox_rounds if philox_rounds is None else philox_rounds
+    sd = spec.rand_seed if seed is None else seed
+    return _Params(num_layers=spec.L, batch=spec.B, num_heads=spec.H, heads_per_group=spec.hpg,
+                   dim=spec.dim, dstate=spec.dstate, max_window=spec.W, ring_len=spec.R,
+                   pad_slot_id=spec.pad_slot_id, philox_rounds=rounds,
+                   state_dtype=DTYPE_CODE[state_dtype or spec.state_dtype],
+                   input_dtype=DTYPE_CODE[spec.input_dtype],
+                   seed=(int(sd) if sd is not None else 0) & 0xFFFFFFFFFFFFFFFF)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def materialize(prob, want_exact: bool = False, state_dtype: Optional[str] = None,
+                philox_rounds: Optional[int] = None, seed: Optional[int] = None):
+    """Run the whole operation on a host problem (``rssm_inputs.Problem``).
+
+    Returns (state_out, scale_out, exact, mag): per-layer copies of the state
+    (and scale) pools with the destination tiles written, and -- when
+    ``want_exact`` -- per-layer fp64 pools holding the unrounded result and the
+    magnitude sum of every written element (NaN elsewhere)."""
+    spec, meta = prob.spec, prob.meta
+    sdt = state_dtype or spec.state_dtype
+    p = params(spec, sdt, philox_rounds, seed)
+    src_arr = np.ascontiguousarray(meta.src, np.int32)
+    dst_arr = np.ascontiguousarray(meta.dst, np.int32)
+    rs = np.ascontiguousarray(meta.ring_start, np.int32)
+    pf = np.ascontiguousarray(meta.prefix, np.int32)
+    ac = np.ascontiguousarray(meta.active, np.int32)
+    state_in = [np.ascontiguousarray(s) for s in prob.state]
+    scale_in = [np.ascontiguousarray(s) for s in prob.scale] if prob.scale else None
+    keep = [state_in, scale_in, prob.x, prob.Bm, prob.dt, prob.A]
+    ins = _Inputs(state=_ptr_array(state_in), state_stride=_i64(meta.state_stride),
+                  scale=_ptr_array(scale_in) if scale_in else None,
+                  scale_stride=_i64(meta.scale_stride),
+                  x=_ptr_array(prob.x), x_stride=_i64(meta.x_stride),
+                  Bm=_ptr_array(prob.Bm), B_stride=_i64(meta.B_stride),
+                  dt=_ptr_array(prob.dt), dt_stride=_i64(meta.dt_stride),
+                  A=_ptr_array(prob.A),
+                  src_slots=src_arr.ctypes.data_as(_P(ctypes.c_int32)),
+                  dst_slots=dst_arr.ctypes.data_as(_P(ctypes.c_int32)),
+                  ring_start=rs.ctypes.data_as(_P(ctypes.c_int32)),
+                  prefix_len=pf.ctypes.data_as(_P(ctypes.c_int32)),
+                  active=ac.ctypes.data_as(_P(ctypes.c_int32)))
+    state_out = [s.copy() for s in state_in]
+    scale_out = [s.copy() for s in scale_in] if scale_in else None
+    exact = mag = None
+    if want_exact or sdt == "f64":
+        exact = [np.full(s.shape, np.nan, np.float64) for s in state_in]
+        mag = [np.full(s.shape, np.nan, np.float64) for s in state_in]
+    outs = _Outputs(state=_ptr_array(state_out),
+                    scale=_ptr_array(scale_out) if scale_out else None,
+                    exact=_ptr_array(exact) if exact else None,
+                    mag=_ptr_array(mag) if mag else None)
+    st = lib().orc_materialize(ctypes.byref(p), ctypes.byref(ins), ctypes.byref(outs))
+    del keep
+    if st != 0:
+        raise OracleError(f"orc_materialize returned {st}")
+    return state_out, scale_out, exact, mag
+
+
+def tile(spec, layer: int, request: int, head: int, ring_start: int, k: int, A_h: float,
+         src_tile: np.ndarray, src_scale: Optional[np.ndarray], x_slot: np.ndarray,
+         B_slot: np.ndarray, dt_slot: np.ndarray, want_codes: bool = True):
+    """One (layer, request, head) tile.  Arrays are the dense per-slot views of
+    the source slot.  Returns (codes, scale, exact, mag)."""
+    p = params(spec)
+    n = spec.dim * spec.dstate
+    src_tile = np.ascontiguousarray(src_tile).reshape(-1)
+    exact = np.empty(n, np.float64)
+    mag = np.empty(n, np.float64)
+    codes = np.empty(n, STORAGE_NP[spec.state_dtype]) if want_codes else None
+    scale = np.empty(spec.dim, np.float32) if src_scale is not None else None
+    args = [np.ascontiguousarray(a) if a is not None else None
+            for a in (src_scale, x_slot, B_slot, dt_slot)]
+    st = lib().orc_tile(ctypes.byref(p), layer, request, head, ring_start, k, float(A_h),
+                        _ptr(src_tile), _ptr(args[0]), _ptr(args[1]), _ptr(args[2]), _ptr(args[3]),
+                        _ptr(exact), _ptr(mag), _ptr(codes), _ptr(scale))
+    if st != 0:
+        raise OracleError(f"orc_tile returned {st}")
+    return codes, scale, exact, mag
+
+
+def encode_row(spec, row: np.ndarray, layer: int, request: int, head: int, r: int,
+               state_dtype: Optional[str] = None, philox_rounds: Optional[int] = None,
+               seed: Optional[int] = None):
+    """Encode one fp32 row (length dstate) into the state dtype."""
+    sdt = state_dtype or spec.state_dtype
+    p = params(spec, sdt, philox_rounds, seed)
+    row = np.ascontiguousarray(row, np.float32)
+    assert row.shape == (spec.dstate,)
+    codes = np.empty(spec.dstate, STORAGE_NP[sdt])
+    scale = np.zeros(1, np.float32)
+    st = lib().orc_encode_row(ctypes.byref(p), _ptr(row), layer, request, head, r, _ptr(codes), _ptr(scale))
+    if st != 0:
+        raise OracleError(f"orc_encode_row returned {st}")
+    return codes, float(scale[0])
+
+
+def round_value(dtype: str, v: float, stochastic: bool = False, u: int = 0) -> int:
+    return int(lib().orc_round_value(DTYPE_CODE[dtype], float(v), 1 if stochastic else 0, int(u) & 0xFFFFFFFF))
+
+
+def decode(dtype: str, codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes).reshape(-1)
+    want = np.dtype(STORAGE_NP[dtype])
+    if codes.dtype != want:
+        if codes.dtype.itemsize != want.itemsize:
+            raise ValueError(f"{dtype} codes need {want.itemsize}-byte items, got {codes.dtype}")
+        codes = codes.view(want)  # reinterpret the bits, never convert values
+    f = lib().orc_decode
+    return np.array([f(DTYPE_CODE[dtype], _ptr(codes), i) for i in range(codes.size)], np.float64)
+
+
+def philox4x32(ctr, key, rounds: int) -> np.ndarray:
+    c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
+    o = (ctypes.c_uint32 * 4)()
+    lib().orc_philox4x32(c, k, int(rounds), o)
+    return np.array(list(o), np.uint32)

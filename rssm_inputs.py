@@ -1,0 +1,366 @@
+"""Seeded synthetic inputs for ReplaySSM prefix materialize.
+
+This module is the only code shared by the CPU oracle (``oracle/``) and the
+HIP path (``replayssm_persistent_rssm_amd``).  It draws inputs and nothing
+else: it holds none of the operation's arithmetic.  Every array is drawn from
+``numpy.random.default_rng(seed)`` (host problems) or a seeded
+``torch.Generator`` on the device (full-size problems that do not fit the
+host), with the shapes and value distributions of the workloads below.
+
+Value distributions (all workloads): state N(0,1); x N(0,1); B N(0, 1/dstate);
+dt U(0.001, 0.1), stored after softplus; A_h = -exp(U(0, ln 16)), so A is in
+[-16, -1].  One-byte state is drawn as an N(0,1) fp32 state and quantized per
+(head, row) with scale = rowmax|S| / qmax (qmax 127 for int8, 448 for e4m3).
+
+Per-slot layouts (dense inside a slot; a slot stride may add a gap):
+  state [H, dim, dstate]     scale [H, dim] fp32
+  x     [R, H, dim]          B     [R, G, dstate]       dt [R, H] fp32
+  A     [H] fp32 per layer
+The ring (x, B, dt) of a request is the one stored in its SOURCE slot.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+DTYPES = ("f32", "bf16", "f16", "i8", "f8e4m3", "f64")
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3, "f8e4m3": 4, "f64": 5}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "f8e4m3": 1, "f64": 8}
+# numpy container used for the raw storage of each dtype
+STORAGE_NP = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16,
+              "i8": np.int8, "f8e4m3": np.uint8, "f64": np.float64}
+QMAX = {"i8": 127.0, "f8e4m3": 448.0}
+
+
+def one_byte(dtype: str) -> bool:
+    return dtype in ("i8", "f8e4m3")
+
+
+@dataclasses.dataclass
+class Spec:
+    """Shape and structure of one workload."""
+    name: str
+    L: int
+    B: int
+    H: int
+    hpg: int
+    dim: int
+    dstate: int
+    R: int
+    W: int
+    state_dtype: str = "bf16"
+    input_dtype: str = "bf16"
+    n_active: Optional[int] = None          # None: all B requests active
+    k_lo: int = 0                           # replay_prefix_len ~ U[k_lo, k_hi]
+    k_hi: int = 8
+    k0_frac: float = 0.0                    # fraction of requests forced to k = 0
+    ring_start: Optional[Sequence[int]] = None   # explicit, else U[0, R)
+    prefix: Optional[Sequence[int]] = None       # explicit, else drawn
+    slots: int = 0                          # state slots per layer (0: 2*B)
+    ring_slots: int = 0                     # ring slots per layer (0: = slots)
+    slot_mode: str = "split"                # "split": src=b, dst=B+perm(b); "perm": disjoint random from pool; "fixed"
+    src_fixed: Optional[Sequence[int]] = None
+    dst_fixed: Optional[Sequence[int]] = None
+    stride_pad: str = "none"                # "none" | "per_layer": + 64*(l+1) elements
+    pad_frac: float = 0.0                   # fraction of (layer, request) pairs with a pad slot
+    pad_slot_id: int = -1
+    philox_rounds: int = 0
+    rand_seed: Optional[int] = None
+    active_order: str = "random"            # "random" | "sorted"
+
+    @property
+    def G(self) -> int:
+        return self.H // self.hpg
+
+
+# The five workloads: a tiny fp32 case, a mid bf16 case, the large hybrid-model
+# shape (48 layers, 256 heads of 64x128, batch 256) with an active-count sweep,
+# an int8 state case and an e4m3 + Philox stochastic-rounding case.
+CONFIGS = {
+    "tiny_f32": Spec("tiny_f32", L=1, B=2, H=4, hpg=2, dim=16, dstate=16, R=8, W=8,
+                     state_dtype="f32", input_dtype="f32", ring_start=[0, 6], prefix=[0, 5],
+                     slots=4, ring_slots=4, slot_mode="fixed", src_fixed=[0, 1], dst_fixed=[2, 3],
+                     active_order="sorted"),
+    "mid_bf16": Spec("mid_bf16", L=4, B=16, H=64, hpg=8, dim=64, dstate=128, R=16, W=8,
+                     state_dtype="bf16", input_dtype="bf16", k_lo=0, k_hi=8,
+                     slots=64, ring_slots=64, slot_mode="perm", stride_pad="per_layer"),
+    "large_bf16": Spec("large_bf16", L=48, B=256, H=256, hpg=32, dim=64, dstate=128, R=16, W=8,
+                       state_dtype="bf16", input_dtype="bf16", n_active=256, k_lo=1, k_hi=8,
+                       slots=512, ring_slots=256, slot_mode="split"),
+    "large_i8": Spec("large_i8", L=48, B=256, H=256, hpg=32, dim=64, dstate=128, R=16, W=8,
+                     state_dtype="i8", input_dtype="f16", n_active=64, k_lo=1, k_hi=8, k0_frac=0.25,
+                     slots=512, ring_slots=256, slot_mode="split"),
+    "large_f8sr": Spec("large_f8sr", L=48, B=256, H=128, hpg=16, dim=64, dstate=128, R=32, W=16,
+                       state_dtype="f8e4m3", input_dtype="bf16", n_active=128, k_lo=0, k_hi=16,
+                       slots=512, ring_slots=256, slot_mode="split", philox_rounds=10, rand_seed=1234),
+}
+
+
+def with_(spec: Spec, **kw) -> Spec:
+    """Copy of a spec with some fields replaced."""
+    return dataclasses.replace(spec, **kw)
+
+
+def scaled(spec: Spec, name: str, **kw) -> Spec:
+    """A smaller workload with the same structure (for full-oracle parity)."""
+    return dataclasses.replace(spec, name=name, **kw)
+
+
+# --------------------------------------------------------------------------
+# Metadata
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class Meta:
+    src: np.ndarray          # (L, B) int32
+    dst: np.ndarray          # (L, B) int32
+    ring_start: np.ndarray   # (B,) int32
+    prefix: np.ndarray       # (B,) int32
+    active: np.ndarray       # (B,) int32
+    state_stride: List[int]  # elements, per layer
+    scale_stride: List[int]
+    x_stride: List[int]
+    B_stride: List[int]
+    dt_stride: List[int]
+    slots: int
+    ring_slots: int
+
+
+def dense_sizes(spec: Spec):
+    """Dense per-slot element counts: state, scale, x, B, dt."""
+    return (spec.H * spec.dim * spec.dstate, spec.H * spec.dim,
+            spec.R * spec.H * spec.dim, spec.R * spec.G * spec.dstate, spec.R * spec.H)
+
+
+def make_meta(spec: Spec, rng: np.random.Generator, n_active: Optional[int] = None) -> Meta:
+    L, B = spec.L, spec.B
+    slots = spec.slots or 2 * B
+    ring_slots = spec.ring_slots or slots
+    n_act = B if (n_active is None and spec.n_active is None) else (spec.n_active if n_active is None else n_active)
+    n_act = int(n_act)
+
+    if spec.ring_start is not None:
+        ring_start = np.asarray(spec.ring_start, np.int32)
+    else:
+        ring_start = rng.integers(0, spec.R, size=B).astype(np.int32)
+    if spec.prefix is not None:
+        prefix = np.asarray(spec.prefix, np.int32)
+    else:
+        prefix = rng.integers(spec.k_lo, spec.k_hi + 1, size=B).astype(np.int32)
+        if spec.k0_frac > 0:
+            n0 = int(round(spec.k0_frac * B))
+            prefix[rng.permutation(B)[:n0]] = 0
+
+    if spec.active_order == "sorted":
+        chosen = np.arange(n_act, dtype=np.int32)
+    else:
+        chosen = rng.permutation(B)[:n_act].astype(np.int32)
+    active = np.full(B, -1, np.int32)
+    active[:n_act] = chosen
+
+    src = np.empty((L, B), np.int32)
+    dst = np.empty((L, B), np.int32)
+    for l in range(L):
+        if spec.slot_mode == "fixed":
+            src[l] = np.asarray(spec.src_fixed, np.int32)
+            dst[l] = np.asarray(spec.dst_fixed, np.int32)
+        elif spec.slot_mode == "perm":
+            perm = rng.permutation(slots)
+            assert slots >= 2 * B and ring_slots >= slots
+            src[l] = perm[:B]
+            dst[l] = perm[B:2 * B]
+        elif spec.slot_mode == "split":
+            assert slots >= 2 * B and ring_slots >= B
+            src[l] = np.arange(B)
+            dst[l] = B + rng.permutation(B)
+        else:
+            raise ValueError(spec.slot_mode)
+    if spec.pad_frac > 0:
+        npad = int(round(spec.pad_frac * L * B))
+        flat = rng.permutation(L * B)[:npad]
+        which = rng.integers(0, 2, size=npad)
+        for f, w in zip(flat, which):
+            (src if w == 0 else dst)[f // B, f % B] = spec.pad_slot_id
+    # Requests that are not listed carry pad slots, as a serving loop would.
+    inactive = np.setdiff1d(np.arange(B), active[:n_act])
+    if len(inactive) and spec.slot_mode == "split":
+        src[:, inactive] = spec.pad_slot_id
+        dst[:, inactive] = spec.pad_slot_id
+
+    d_state, d_scale, d_x, d_B, d_dt = dense_sizes(spec)
+    pad = [64 * (l + 1) if spec.stride_pad == "per_layer" else 0 for l in range(L)]
+    return Meta(src=src, dst=dst, ring_start=ring_start, prefix=prefix, active=active,
+                state_stride=[d_state + p for p in pad], scale_stride=[d_scale + p for p in pad],
+                x_stride=[d_x + p for p in pad], B_stride=[d_B + p for p in pad],
+                dt_stride=[d_dt + p for p in pad], slots=slots, ring_slots=ring_slots)
+
+
+# --------------------------------------------------------------------------
+# Host problems (numpy)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class Problem:
+    spec: Spec
+    meta: Meta
+    state: List[np.ndarray]            # per layer (slots, state_stride), storage dtype
+    scale: Optional[List[np.ndarray]]  # per layer (slots, scale_stride) fp32, 1-byte state only
+    x: List[np.ndarray]                # per layer (ring_slots, x_stride)
+    Bm: List[np.ndarray]
+    dt: List[np.ndarray]               # fp32
+    A: List[np.ndarray]                # (H,) fp32
+
+    @property
+    def rand_seed(self) -> Optional[int]:
+        return self.spec.rand_seed
+
+
+def _to_storage(vals: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 values -> raw storage (library casts, nearest-even)."""
+    if dtype == "f32":
+        return vals.astype(np.float32)
+    if dtype == "f64":
+        return vals.astype(np.float64)
+    if dtype == "f16":
+        return vals.astype(np.float16)
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(vals, dtype=np.float32))
+    if dtype == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if dtype == "f8e4m3":
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    raise ValueError(dtype)
+
+
+def _quantized_rows(S: np.ndarray, dtype: str):
+    """Per-row symmetric quantization of an fp32 state (input recipe only)."""
+    qmax = np.float32(QMAX[dtype])
+    rowmax = np.abs(S).max(axis=-1, keepdims=True).astype(np.float32)
+    scale = (rowmax / qmax).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1))
+    t = (S / safe).astype(np.float32)
+    if dtype == "i8":
+        codes = np.clip(np.rint(t), -127, 127).astype(np.int8)
+    else:
+        codes = _to_storage(np.clip(t, -448, 448), "f8e4m3")
+    return codes, scale[..., 0]
+
+
+def _draw_state(rng, spec: Spec, n_slots: int, stride: int):
+    """State pool of one layer: every slot and gap holds drawn values."""
+    dense = spec.H * spec.dim * spec.dstate
+    if one_byte(spec.state_dtype):
+        S = rng.standard_normal((n_slots, spec.H, spec.dim, spec.dstate), dtype=np.float32)
+        codes, scale = _quantized_rows(S, spec.state_dtype)
+        pool = rng.integers(-100, 100, size=(n_slots, stride)).astype(STORAGE_NP[spec.state_dtype]) \
+            if spec.state_dtype == "i8" else rng.integers(0, 0x7E, size=(n_slots, stride)).astype(np.uint8)
+        pool[:, :dense] = codes.reshape(n_slots, dense)
+        d_scale = spec.H * spec.dim
+        sstride = stride - dense + d_scale
+        spool = rng.random((n_slots, sstride), dtype=np.float32)
+        spool[:, :d_scale] = scale.reshape(n_slots, d_scale)
+        return pool, spool
+    vals = rng.standard_normal((n_slots, stride), dtype=np.float32)
+    return _to_storage(vals, spec.state_dtype), None
+
+
+def make_problem(spec: Spec, seed: int, n_active: Optional[int] = None) -> Problem:
+    """Host (numpy) problem: every pool fully drawn, including gaps and dst slots."""
+    rng = np.random.default_rng(seed)
+    meta = make_meta(spec, rng, n_active)
+    state, scale, xs, Bs, dts, As = [], [], [], [], [], []
+    for l in range(spec.L):
+        st, sc = _draw_state(rng, spec, meta.slots, meta.state_stride[l])
+        state.append(st)
+        if sc is not None:
+            assert sc.shape[1] == meta.scale_stride[l]
+            scale.append(sc)
+        xv = rng.standard_normal((meta.ring_slots, meta.x_stride[l]), dtype=np.float32)
+        xs.append(_to_storage(xv, spec.input_dtype))
+        bv = rng.standard_normal((meta.ring_slots, meta.B_stride[l]), dtype=np.float32) / np.float32(math.sqrt(spec.dstate))
+        Bs.append(_to_storage(bv, spec.input_dtype))
+        dts.append(rng.uniform(0.001, 0.1, size=(meta.ring_slots, meta.dt_stride[l])).astype(np.float32))
+        As.append((-np.exp(rng.uniform(0.0, math.log(16.0), size=spec.H))).astype(np.float32))
+    return Problem(spec=spec, meta=meta, state=state, scale=scale if scale else None,
+                   x=xs, Bm=Bs, dt=dts, A=As)
+
+
+# --------------------------------------------------------------------------
+# Device problems (torch), for workloads too large for host memory
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class DeviceProblem:
+    spec: Spec
+    meta: Meta
+    state: list      # per layer torch tensors (slots, stride), raw storage dtype
+    scale: Optional[list]
+    x: list
+    Bm: list
+    dt: list
+    A: list
+
+
+def _torch_storage(dtype: str):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+            "i8": torch.int8, "f8e4m3": torch.uint8}[dtype]
+
+
+def make_device_problem(spec: Spec, seed: int, device="cuda", n_active: Optional[int] = None,
+                        fill_dst: int = 0xA5) -> DeviceProblem:
+    """Device problem drawn with a seeded torch generator.  Only source slots
+    (and the ring) get random values; every other slot is filled with the byte
+    `fill_dst`, so that untouched slots can be recognised."""
+    import torch
+    rng = np.random.default_rng(seed)
+    meta = make_meta(spec, rng, n_active)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    src_slots = np.unique(meta.src[meta.src != spec.pad_slot_id]) if (meta.src != spec.pad_slot_id).any() else np.zeros(0, np.int64)
+    lo_src = int(src_slots.min()) if len(src_slots) else 0
+    hi_src = int(src_slots.max()) + 1 if len(src_slots) else 0
+    dense = spec.H * spec.dim * spec.dstate
+    sdt = _torch_storage(spec.state_dtype)
+    idt = _torch_storage(spec.input_dtype)
+    state, scale, xs, Bs, dts, As = [], [], [], [], [], []
+    for l in range(spec.L):
+        st = torch.empty((meta.slots, meta.state_stride[l]), dtype=sdt, device=device)
+        st.view(torch.uint8).fill_(fill_dst)
+        sc = None
+        if one_byte(spec.state_dtype):
+            sc = torch.empty((meta.slots, meta.scale_stride[l]), dtype=torch.float32, device=device)
+            sc.view(torch.uint8).fill_(fill_dst)
+            qmax = QMAX[spec.state_dtype]
+            # quantize one source slot range at a time to bound temporaries
+            for s0 in range(lo_src, hi_src, 32):
+                s1 = min(hi_src, s0 + 32)
+                S = torch.randn((s1 - s0, spec.H, spec.dim, spec.dstate), generator=g, device=device,
+                                dtype=torch.float32)
+                rowmax = S.abs().amax(dim=-1, keepdim=True)
+                sca = rowmax / qmax
+                t = S / torch.where(sca > 0, sca, torch.ones_like(sca))
+                if spec.state_dtype == "i8":
+                    codes = torch.clamp(torch.round(t), -127, 127).to(torch.int8)
+                else:
+                    codes = torch.clamp(t, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+                st[s0:s1, :dense] = codes.reshape(s1 - s0, dense)
+                sc[s0:s1, :spec.H * spec.dim] = sca.reshape(s1 - s0, spec.H * spec.dim)
+                del S, rowmax, sca, t, codes
+        else:
+            for s0 in range(lo_src, hi_src, 64):
+                s1 = min(hi_src, s0 + 64)
+                st[s0:s1, :dense] = torch.randn((s1 - s0, dense), generator=g, device=device, dtype=sdt)
+        state.append(st)
+        if sc is not None:
+            scale.append(sc)
+        xs.append(torch.randn((meta.ring_slots, meta.x_stride[l]), generator=g, device=device, dtype=idt))
+        Bs.append(torch.randn((meta.ring_slots, meta.B_stride[l]), generator=g, device=device,
+                              dtype=torch.float32).mul_(1.0 / math.sqrt(spec.dstate)).to(idt))
+        dts.append(torch.rand((meta.ring_slots, meta.dt_stride[l]), generator=g, device=device,
+                              dtype=torch.float32).mul_(0.099).add_(0.001))
+        As.append(-torch.exp(torch.rand((spec.H,), generator=g, device=device, dtype=torch.float32)
+                             * math.log(16.0)))
+    return DeviceProblem(spec=spec, meta=meta, state=state, scale=scale if scale else None,
+                         x=xs, Bm=Bs, dt=dts, A=As)
+

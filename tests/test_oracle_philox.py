@@ -1,0 +1,60 @@
+"""Oracle Philox4x32 pinned to rocRAND's independent Philox4x32-10.
+
+The stochastic-rounding key mapping (seed -> key, coordinates -> counter) is
+the library's own reading; the generator itself is the published
+Philox4x32-R of Salmon, Moraes, Dror and Shaw (SC'11).  rocRAND ships a
+separate implementation of the 10-round variant; it is compiled here on the
+host and called on the same (counter, key) pairs.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROCRAND_INC = "/opt/rocm/include"
+
+
+@pytest.fixture(scope="module")
+def rocrand_ref(tmp_path_factory):
+    if not os.path.exists(os.path.join(ROCRAND_INC, "rocrand", "rocrand_philox4x32_10.h")):
+        pytest.fail("rocRAND headers are missing; the Philox pin needs them")
+    exe = str(tmp_path_factory.mktemp("philox") / "rocrand_philox_ref")
+    cxx = shutil.which("g++")
+    subprocess.check_call([cxx, "-O1", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I" + ROCRAND_INC,
+                           os.path.join(HERE, "pins", "rocrand_philox_ref.cpp"), "-o", exe])
+
+    def run(rows):
+        text = "".join("%08x %08x %08x %08x %08x %08x\n" % tuple(int(v) for v in r) for r in rows)
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
+        return np.array([[int(w, 16) for w in line.split()] for line in out.strip().splitlines()], np.uint64)
+    return run
+
+
+def test_philox10_matches_rocrand(orc, rocrand_ref):
+    rng = np.random.default_rng(7)
+    rows = rng.integers(0, 2**32, size=(500, 6), dtype=np.uint64)
+    # plus edge words: all zero, all ones, small counters like the SR mapping uses
+    rows = np.vstack([rows, [[0] * 6, [0xFFFFFFFF] * 6, [1, 2, 3, 4, 1234, 0], [31, 127, 255, 47, 1234, 0]]])
+    ref = rocrand_ref(rows)
+    got = np.array([orc.philox4x32(r[:4], r[4:], 10) for r in rows], np.uint64)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_philox_zero_rounds_is_identity(orc):
+    assert list(orc.philox4x32([1, 2, 3, 4], [5, 6], 0)) == [1, 2, 3, 4]
+
+
+def test_philox_rounds_change_output(orc):
+    a = orc.philox4x32([9, 8, 7, 6], [5, 4], 7)
+    b = orc.philox4x32([9, 8, 7, 6], [5, 4], 10)
+    assert list(a) != list(b)
+
+
+def test_philox_output_is_uniform(orc):
+    # 32-bit words over many counters: mean of u/2^32 near 1/2, each bit ~ 1/2.
+    words = np.concatenate([orc.philox4x32([i, 0, 0, 0], [1234, 0], 10) for i in range(2000)]).astype(np.float64)
+    u = words / 2.0**32
+    assert abs(u.mean() - 0.5) < 4 * np.sqrt(1 / 12 / u.size)
