@@ -1,0 +1,250 @@
+"""Benchmark: ReplaySSM prefix materialize on one MI355X.
+
+Workload (the pages' hybrid-model shape): 48 layers, physical batch 256,
+256 heads per layer in 8 B groups, 64x128 state per head, bf16 state/x/B,
+fp32 dt/A, 16-entry ring, max_window 8, replay_prefix_len ~ U[1, 8].
+Inputs are synthetic (seeded device generator) and resident in HBM before
+timing starts.  One step = one call with all 256 requests active.
+
+Printed JSON line: "value" is the achieved algorithmic HBM throughput in GB/s
+of the full-batch call (bytes the method must move -- state in and out plus
+the replayed x/B/dt rows -- divided by the measured time per call).  Extra
+fields: the active-count sweep {0, 1, 16, 256} (ms/call, GB/s, us/request),
+the empty-launch cost (events over back-to-back calls, and graph replay), a
+roofline object for the kernel, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+WORKLOAD = "large_bf16"
+SEED = 1002
+KERNEL_SOURCES = ["replayssm_persistent_rssm_amd/csrc/rssm_kernel.h",
+                  "replayssm_persistent_rssm_amd/csrc/rssm_device.h"]
+
+
+def say(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(bytes_alg: int):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "materialize_large_bf16_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def timed_calls(fn, n, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    stop.record(stream)
+    stop.synchronize()
+    return start.elapsed_time(stop) / n  # ms per call
+
+
+def cpu_baseline(dp, seconds: float):
+    """The CPU oracle on a bounded sample of the same workload: consecutive
+    layers of the first listed request, every head, until `seconds` pass."""
+    import oracle
+    import rssm_inputs as ri
+    import torch
+    spec, m = dp.spec, dp.meta
+    b = int(m.active[0])
+    n_tile = spec.dim * spec.dstate
+    _, _, d_x, d_B, d_dt = ri.dense_sizes(spec)
+    sb, ib = ri.ELEM_BYTES[spec.state_dtype], ri.ELEM_BYTES[spec.input_dtype]
+    k, r0 = int(m.prefix[b]), int(m.ring_start[b])
+    done_bytes, spent, tiles, layers = 0, 0.0, 0, 0
+    for l in range(spec.L):
+        s = int(m.src[l, b])
+        host = lambda t: (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy()  # noqa: E731
+        src = host(dp.state[l][s, :spec.H * n_tile]).view(np.uint16)
+        x = host(dp.x[l][s, :d_x]).view(np.uint16)
+        B = host(dp.Bm[l][s, :d_B]).view(np.uint16)
+        dt = dp.dt[l][s, :d_dt].cpu().numpy()
+        A = dp.A[l].cpu().numpy()
+        t0 = time.perf_counter()
+        for h in range(spec.H):
+            oracle.tile(spec, l, b, h, r0, k, float(A[h]), src[h * n_tile:(h + 1) * n_tile], None, x, B, dt)
+        spent += time.perf_counter() - t0
+        tiles += spec.H
+        layers += 1
+        done_bytes += 2 * spec.H * n_tile * sb + k * (spec.H * spec.dim * ib + spec.G * spec.dstate * ib + spec.H * 4)
+        if spent >= seconds:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"request {b} (k={k}), layers 0..{layers - 1}, all {spec.H} heads: {tiles} tiles of "
+                      f"{spec.dim}x{spec.dstate}, {done_bytes} algorithmic bytes in {spent:.1f} s, single thread",
+            "seconds": round(spent, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--only-main", action="store_true", help="profile mode: warmup + timed steps only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path needs no collectives and every run here uses a "
+              "single MI355X; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    import replayssm_persistent_rssm_amd as rp
+
+    dev = torch.device("cuda:0")
+    spec = ri.CONFIGS[WORKLOAD]
+    say("generating", WORKLOAD, "seed", SEED)
+    t0 = time.time()
+    dp = ri.make_device_problem(spec, SEED, dev, n_active=spec.B, fill_dst=0)
+    tabs = hx.tables(dp, dev)
+    torch.cuda.synchronize()
+    say(f"inputs resident in HBM ({time.time() - t0:.1f} s)")
+    stream = torch.cuda.current_stream()
+    grid, block, lds = rp.rssm_materialize_launch_config(
+        num_layers=spec.L, batch=spec.B, num_heads=spec.H, heads_per_group=spec.hpg, dim=spec.dim,
+        dstate=spec.dstate, max_window=spec.W, ring_buffer_len=spec.R, state_dtype=spec.state_dtype,
+        input_dtype=spec.input_dtype)
+
+    full_bytes = hx.algorithmic_bytes(spec, dp.meta)
+    call = lambda act=None: hx.materialize(dp, tabs, active=act)  # noqa: E731
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = timed_calls(call, args.steps, stream)
+    torch.cuda.synchronize()
+    value = full_bytes / (ms * 1e-3) / 1e9
+    say(f"full batch: {ms:.3f} ms/call, {value:.1f} GB/s")
+    result = {
+        "metric": "materialize HBM GB/s (% of roofline) + us/request at L=48,H=256; empty-launch us",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded device generator; no dataset)",
+        "config": {"workload": "large_bf16: L=48, B=256 (256 active), H=256 (8 groups), state 64x128, "
+                               "bf16 state/x/B, fp32 dt/A, R=16, max_window=8, k~U[1,8]",
+                   "storage": "bf16", "accumulate": "f32", "grid": grid, "block": block, "lds_bytes": lds,
+                   "algorithmic_bytes_per_call": full_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(full_bytes),
+                     "kernel": "materialize_kernel<bf16,bf16,64x128,kmax8>", "kernel_source_hash": kernel_hash()},
+        "us_per_request_full": round(ms * 1e3 / spec.B, 3),
+    }
+    if args.only_main:
+        print(json.dumps(result), flush=True)
+        return
+
+    if not args.no_sweep:
+        rng = np.random.default_rng(SEED)
+        perm = rng.permutation(spec.B).astype(np.int32)
+
+        def active_list(ids):
+            a = np.full(spec.B, -1, np.int32)
+            a[:len(ids)] = ids
+            return torch.from_numpy(a).to(dev)
+
+        sweep = {}
+        t_empty = None
+        for n, reps in ((0, 1000), (1, 64), (16, 32), (256, max(4, args.steps // 2))):
+            # rotate the active set so the 256 MB last-level cache cannot serve it
+            n_sets = 1 if n in (0, 256) else min(32, spec.B // n)
+            sets = [active_list(perm[(j * n) % spec.B:(j * n) % spec.B + n]) for j in range(n_sets)]
+            it = [0]
+
+            def rot():
+                call(sets[it[0] % n_sets])
+                it[0] += 1
+            for _ in range(3):
+                rot()
+            torch.cuda.synchronize()
+            ms_n = timed_calls(rot, reps, stream)
+            ids = [int(v) for v in sets[0].cpu().numpy()[:n]]
+            meta_n = dp.meta
+            bytes_n = hx.algorithmic_bytes(spec, ri.Meta(**{**meta_n.__dict__, "active": np.array(
+                ids + [-1] * (spec.B - n), np.int32)})) if n else 0
+            if n_sets > 1:  # mean over the rotated sets
+                tot = 0
+                for sset in sets:
+                    ids_s = [int(v) for v in sset.cpu().numpy()[:n]]
+                    tot += hx.algorithmic_bytes(spec, ri.Meta(**{**meta_n.__dict__, "active": np.array(
+                        ids_s + [-1] * (spec.B - n), np.int32)}))
+                bytes_n = tot // n_sets
+            if n == 0:
+                t_empty = ms_n
+            entry = {"ms_per_call": round(ms_n, 5), "algorithmic_bytes": bytes_n}
+            if n:
+                entry["GB/s"] = round(bytes_n / (ms_n * 1e-3) / 1e9, 1)
+                entry["frac_of_hbm_peak"] = round(bytes_n / (ms_n * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                entry["us_per_request"] = round(ms_n * 1e3 / n, 3)
+                entry["us_per_request_slope"] = round((ms_n - t_empty) * 1e3 / n, 3)
+            sweep[str(n)] = entry
+            say(f"active={n}: {entry}")
+        result["sweep_active"] = sweep
+        result["empty_launch_us"] = round(t_empty * 1e3, 3)
+
+        # empty launch under graph replay (100 captured calls)
+        empty = active_list([])
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call(empty)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(100):
+                call(empty)
+        g.replay()
+        torch.cuda.synchronize()
+        t_graph = timed_calls(g.replay, 10, stream) / 100
+        result["empty_launch_us_graph"] = round(t_graph * 1e3, 3)
+        say(f"empty launch: {t_empty * 1e3:.2f} us (stream), {t_graph * 1e3:.2f} us (graph)")
+
+    if not args.no_cpu_baseline:
+        say(f"CPU oracle sample (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(dp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

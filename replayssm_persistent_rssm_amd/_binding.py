@@ -1,0 +1,249 @@
+"""ctypes binding of librssm_materialize (argument marshalling only).
+
+Every entry point has the C name from ``include/rssm_materialize.h``.  Torch
+supplies device memory and streams; the binding checks host-visible tensor
+metadata (device, dtype, shape, contiguity), converts tensors to device
+addresses and calls the library.  There is no CPU fallback: if the library is
+missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librssm_materialize.so")
+
+RSSM_F32, RSSM_BF16, RSSM_F16, RSSM_I8, RSSM_F8E4M3 = 0, 1, 2, 3, 4
+RSSM_OK, RSSM_ERR_INVALID_ARGUMENT, RSSM_ERR_UNSUPPORTED, RSSM_ERR_HIP = 0, 1, 2, 3
+EXPORTS = ("rssm_materialize", "rssm_last_error", "rssm_materialize_launch_config", "rssm_debug_encode_rows")
+_INT32_MAX = 2**31 - 1
+
+
+class RssmError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"rssm status {status}: {message}")
+        self.status = status
+
+
+class RssmDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_layers", "batch", "num_heads", "heads_per_group", "dim", "dstate", "max_window",
+        "ring_buffer_len", "pad_slot_id", "philox_rounds", "state_dtype", "input_dtype", "a_dtype",
+        "max_workgroups")]
+
+
+_I64P = ctypes.c_void_p
+_I32P = ctypes.c_void_p
+
+
+class RssmTables(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "state_ptrs", "state_slot_strides", "x_ptrs", "x_slot_strides", "B_ptrs", "B_slot_strides",
+        "dt_ptrs", "dt_slot_strides", "A_ptrs", "scale_ptrs", "scale_slot_strides", "src_slots", "dst_slots",
+        "ring_start", "replay_prefix_len", "active_request_indices", "rand_seed")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built. Build it with `python -m replayssm_persistent_rssm_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path.")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.rssm_materialize.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(RssmTables), ctypes.c_void_p]
+    lib.rssm_materialize.restype = ctypes.c_int
+    lib.rssm_last_error.argtypes = []
+    lib.rssm_last_error.restype = ctypes.c_char_p
+    lib.rssm_materialize_launch_config.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(ctypes.c_int32),
+                                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.rssm_materialize_launch_config.restype = ctypes.c_int
+    lib.rssm_debug_encode_rows.argtypes = [ctypes.POINTER(RssmDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_void_p]
+    lib.rssm_debug_encode_rows.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def rssm_last_error() -> str:
+    return _lib.rssm_last_error().decode()
+
+
+def _check(status: int):
+    if status != RSSM_OK:
+        raise RssmError(status, rssm_last_error())
+
+
+_NAMES = {"f32": RSSM_F32, "float32": RSSM_F32, "bf16": RSSM_BF16, "bfloat16": RSSM_BF16,
+          "f16": RSSM_F16, "float16": RSSM_F16, "i8": RSSM_I8, "int8": RSSM_I8,
+          "f8e4m3": RSSM_F8E4M3, "float8_e4m3fn": RSSM_F8E4M3}
+
+
+def dtype_code(dt) -> int:
+    """Library dtype code from a name ('bf16', ...), a torch dtype or a code."""
+    if isinstance(dt, int):
+        return dt
+    if isinstance(dt, str):
+        if dt not in _NAMES:
+            raise ValueError(f"unsupported dtype {dt!r}")
+        return _NAMES[dt]
+    name = str(dt).replace("torch.", "")
+    if name in _NAMES:
+        return _NAMES[name]
+    raise ValueError(f"unsupported dtype {dt!r}")
+
+
+def _scalar(name: str, v: int) -> int:
+    v = int(v)
+    if not (-_INT32_MAX - 1 <= v <= _INT32_MAX):
+        raise ValueError(f"{name}={v} does not fit the library's int32 parameter")
+    return v
+
+
+def make_desc(*, num_layers, batch, num_heads, heads_per_group, dim, dstate, max_window, ring_buffer_len,
+              state_dtype, input_dtype="bf16", matrixA_dtype="f32", pad_slot_id=-1, philox_rounds=0,
+              max_workgroups=0) -> RssmDesc:
+    return RssmDesc(num_layers=_scalar("num_layers", num_layers), batch=_scalar("batch", batch),
+                    num_heads=_scalar("num_heads", num_heads),
+                    heads_per_group=_scalar("heads_per_group", heads_per_group),
+                    dim=_scalar("dim", dim), dstate=_scalar("dstate", dstate),
+                    max_window=_scalar("max_window", max_window),
+                    ring_buffer_len=_scalar("ring_buffer_len", ring_buffer_len),
+                    pad_slot_id=_scalar("pad_slot_id", pad_slot_id),
+                    philox_rounds=_scalar("philox_rounds", philox_rounds),
+                    state_dtype=dtype_code(state_dtype), input_dtype=dtype_code(input_dtype),
+                    a_dtype=dtype_code(matrixA_dtype), max_workgroups=_scalar("max_workgroups", max_workgroups))
+
+
+def _ptr(t, name: str, dtype=None, shape=None):
+    """Device address of a torch tensor after host-side metadata checks."""
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def rssm_materialize(state_ptrs, state_slot_strides, x_cache_ptrs, x_cache_slot_strides, B_cache_ptrs,
+                     B_cache_slot_strides, dt_cache_ptrs, dt_cache_slot_strides, A_ptrs, state_scale_ptrs,
+                     state_scale_slot_strides, src_slots, dst_slots, ring_start, replay_prefix_len,
+                     active_request_indices, *, state_dtype, input_dtype, matrixA_dtype, dim: int, dstate: int,
+                     num_heads: int, heads_per_group: int, max_window: int, ring_buffer_len: int,
+                     pad_slot_id: int = -1, rand_seed=None, philox_rounds: int = 0, max_workgroups: int = 0,
+                     stream=None) -> None:
+    """Enqueue one materialize call (keyword names of the page's signature).
+
+    Per-layer tables are device int64 tensors of shape (L,); src_slots and
+    dst_slots device int32 (L, B); ring_start, replay_prefix_len and
+    active_request_indices device int32 (B,); rand_seed a device int64 (1,)
+    tensor.  Enqueued on `stream` (default: torch's current stream)."""
+    import torch
+    L = int(state_ptrs.shape[0])
+    Bsz = int(ring_start.shape[0])
+    desc = make_desc(num_layers=L, batch=Bsz, num_heads=num_heads, heads_per_group=heads_per_group, dim=dim,
+                     dstate=dstate, max_window=max_window, ring_buffer_len=ring_buffer_len,
+                     state_dtype=state_dtype, input_dtype=input_dtype, matrixA_dtype=matrixA_dtype,
+                     pad_slot_id=pad_slot_id, philox_rounds=philox_rounds, max_workgroups=max_workgroups)
+    i64, i32 = torch.int64, torch.int32
+    quant = desc.state_dtype in (RSSM_I8, RSSM_F8E4M3)
+    tab = RssmTables(
+        state_ptrs=_ptr(state_ptrs, "state_ptrs", i64, (L,)),
+        state_slot_strides=_ptr(state_slot_strides, "state_slot_strides", i64, (L,)),
+        x_ptrs=_ptr(x_cache_ptrs, "x_cache_ptrs", i64, (L,)),
+        x_slot_strides=_ptr(x_cache_slot_strides, "x_cache_slot_strides", i64, (L,)),
+        B_ptrs=_ptr(B_cache_ptrs, "B_cache_ptrs", i64, (L,)),
+        B_slot_strides=_ptr(B_cache_slot_strides, "B_cache_slot_strides", i64, (L,)),
+        dt_ptrs=_ptr(dt_cache_ptrs, "dt_cache_ptrs", i64, (L,)),
+        dt_slot_strides=_ptr(dt_cache_slot_strides, "dt_cache_slot_strides", i64, (L,)),
+        A_ptrs=_ptr(A_ptrs, "A_ptrs", i64, (L,)),
+        scale_ptrs=_ptr(state_scale_ptrs, "state_scale_ptrs", i64, (L,)) if quant or state_scale_ptrs is not None else None,
+        scale_slot_strides=_ptr(state_scale_slot_strides, "state_scale_slot_strides", i64, (L,))
+        if quant or state_scale_slot_strides is not None else None,
+        src_slots=_ptr(src_slots, "src_slots", i32, (L, Bsz)),
+        dst_slots=_ptr(dst_slots, "dst_slots", i32, (L, Bsz)),
+        ring_start=_ptr(ring_start, "ring_start", i32, (Bsz,)),
+        replay_prefix_len=_ptr(replay_prefix_len, "replay_prefix_len", i32, (Bsz,)),
+        active_request_indices=_ptr(active_request_indices, "active_request_indices", i32, (Bsz,)),
+        rand_seed=_ptr(rand_seed, "rand_seed", i64, (1,)) if rand_seed is not None else None)
+    _check(_lib.rssm_materialize(ctypes.byref(desc), ctypes.byref(tab), _stream_handle(stream)))
+
+
+# The page's name for the same call.
+replayssm_materialize = rssm_materialize
+
+
+def rssm_materialize_launch_config(**desc_kw):
+    """(grid, block, lds_bytes) the library would launch for these scalars."""
+    desc = make_desc(**desc_kw)
+    g, b, s = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.rssm_materialize_launch_config(ctypes.byref(desc), ctypes.byref(g), ctypes.byref(b),
+                                               ctypes.byref(s)))
+    return g.value, b.value, s.value
+
+
+def rssm_debug_encode_rows(rows, coords, rand_seed, out_codes, out_scales, *, state_dtype, dstate: int,
+                           philox_rounds: int = 0, stream=None) -> None:
+    """Run the kernel's encode step on fp32 rows [n, dstate] (test hook)."""
+    import torch
+    n = int(rows.shape[0])
+    desc = make_desc(num_layers=1, batch=1, num_heads=1, heads_per_group=1, dim=64, dstate=dstate,
+                     max_window=1, ring_buffer_len=1, state_dtype=state_dtype, philox_rounds=philox_rounds)
+    _check(_lib.rssm_debug_encode_rows(
+        ctypes.byref(desc), _ptr(rows, "rows", torch.float32, (n, dstate)),
+        _ptr(coords, "coords", torch.int32, (n, 4)) if coords is not None else None,
+        _ptr(rand_seed, "rand_seed", torch.int64, (1,)) if rand_seed is not None else None,
+        _ptr(out_codes, "out_codes"), _ptr(out_scales, "out_scales") if out_scales is not None else None,
+        n, _stream_handle(stream)))
+
+
+def pointer_table(tensors: Sequence, device) -> "torch.Tensor":
+    """Device int64 table of the base addresses of per-layer tensors."""
+    import torch
+    return torch.tensor([int(t.data_ptr()) for t in tensors], dtype=torch.int64, device=device)
+
+
+def stride_table(strides: Sequence[int], device) -> "torch.Tensor":
+    import torch
+    return torch.tensor([int(s) for s in strides], dtype=torch.int64, device=device)
+
+
+def checkpoint_prefix_len(materialized_pos: int, buffered: int, period: int) -> Optional[int]:
+    """replay_prefix_len a prefix cache passes to write its next checkpoint.
+
+    The source state is the state after token `materialized_pos`; the ring
+    holds `buffered` further accepted tokens; checkpoints are kept every
+    `period` tokens.  Returns the number of ring entries up to the next
+    multiple of `period`, or None when the ring does not reach it (caller
+    policy from the materialize documentation's Notes and the pull request's
+    Description; the kernel itself has no such logic)."""
+    if period <= 0 or buffered < 0 or materialized_pos < 0:
+        raise ValueError("period must be > 0; positions and counts >= 0")
+    to_boundary = period - (materialized_pos % period)
+    return to_boundary if to_boundary <= buffered else None

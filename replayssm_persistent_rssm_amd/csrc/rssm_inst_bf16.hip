@@ -1,0 +1,59 @@
+// rssm_inst_bf16.hip -- compiled instances of the materialize and encode
+// kernels for bf16 state (one translation unit per state dtype so they build
+// in parallel).
+#include "rssm_kernel.h"
+
+namespace rssm {
+
+#define RSSM_KENTRY(ST, IT, D, S, KM, SR)                                              \
+  {ST, IT, D, S, KM, SR, reinterpret_cast<const void*>(&materialize_kernel<ST, IT, D, S, KM, (SR != 0)>), \
+   "materialize<" #ST "," #IT "," #D "x" #S ",kmax" #KM ",sr" #SR ">"},
+#define RSSM_EENTRY(ST, S, SR)                                                           \
+  {ST, S, SR, reinterpret_cast<const void*>(&encode_rows_kernel<ST, S, (SR != 0)>),     \
+   "encode_rows<" #ST ",dstate" #S ",sr" #SR ">"},
+
+static const KernelEntry kKernels[] = {
+    RSSM_KENTRY(kBF16, kF32, 16, 16, 8, 0)
+    RSSM_KENTRY(kBF16, kF32, 16, 16, 8, 1)
+    RSSM_KENTRY(kBF16, kF32, 16, 16, 16, 0)
+    RSSM_KENTRY(kBF16, kF32, 16, 16, 16, 1)
+    RSSM_KENTRY(kBF16, kBF16, 16, 16, 8, 0)
+    RSSM_KENTRY(kBF16, kBF16, 16, 16, 8, 1)
+    RSSM_KENTRY(kBF16, kBF16, 16, 16, 16, 0)
+    RSSM_KENTRY(kBF16, kBF16, 16, 16, 16, 1)
+    RSSM_KENTRY(kBF16, kF16, 16, 16, 8, 0)
+    RSSM_KENTRY(kBF16, kF16, 16, 16, 8, 1)
+    RSSM_KENTRY(kBF16, kF16, 16, 16, 16, 0)
+    RSSM_KENTRY(kBF16, kF16, 16, 16, 16, 1)
+    RSSM_KENTRY(kBF16, kF32, 64, 128, 8, 0)
+    RSSM_KENTRY(kBF16, kF32, 64, 128, 8, 1)
+    RSSM_KENTRY(kBF16, kF32, 64, 128, 16, 0)
+    RSSM_KENTRY(kBF16, kF32, 64, 128, 16, 1)
+    RSSM_KENTRY(kBF16, kBF16, 64, 128, 8, 0)
+    RSSM_KENTRY(kBF16, kBF16, 64, 128, 8, 1)
+    RSSM_KENTRY(kBF16, kBF16, 64, 128, 16, 0)
+    RSSM_KENTRY(kBF16, kBF16, 64, 128, 16, 1)
+    RSSM_KENTRY(kBF16, kF16, 64, 128, 8, 0)
+    RSSM_KENTRY(kBF16, kF16, 64, 128, 8, 1)
+    RSSM_KENTRY(kBF16, kF16, 64, 128, 16, 0)
+    RSSM_KENTRY(kBF16, kF16, 64, 128, 16, 1)
+};
+
+static const EncodeEntry kEncoders[] = {
+    RSSM_EENTRY(kBF16, 16, 0)
+    RSSM_EENTRY(kBF16, 16, 1)
+    RSSM_EENTRY(kBF16, 128, 0)
+    RSSM_EENTRY(kBF16, 128, 1)
+};
+
+const KernelEntry* kernels_bf16(int* n) {
+  *n = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
+  return kKernels;
+}
+
+const EncodeEntry* encoders_bf16(int* n) {
+  *n = static_cast<int>(sizeof(kEncoders) / sizeof(kEncoders[0]));
+  return kEncoders;
+}
+
+}  // namespace rssm

@@ -1,0 +1,458 @@
+// rssm_kernel.h -- persistent gfx950 kernel for ReplaySSM prefix materialize.
+//
+// Operation: flashinfer.mamba.replayssm_materialize (documentation page,
+// Summary and Parameters).  For each request listed in the -1-terminated
+// active list, each layer whose source and destination slots are not the pad
+// sentinel, and each head h, with k = replay_prefix_len[b] ring entries
+// e_j = (ring_start[b] + j) mod R taken from the SOURCE slot's ring:
+//     S' = D * S + sum_j w_j * x_j (outer) B_j
+//     a_j = exp(dt_j * A_h),  D = prod_j a_j,  w_j = dt_j * prod_{u>j} a_u
+// which is the token-by-token recurrence S <- a_j S + dt_j x_j B_j^T unrolled.
+// k = 0 copies the state (and scale) bytes exactly.
+//
+// Design (MI355X, wave64):
+//  * Persistent grid; the -1-terminated active list is scanned once per
+//    wavefront (ballot), so a call with no active request costs one launch in
+//    which every wave does one load and exits (the pull-request page's reason
+//    for persistent kernels and the active list).
+//  * Work item = one (active request, layer, head) tile of dim x dstate.  Each
+//    wavefront owns a contiguous range of items (request-major, then layer,
+//    then head), so consecutive items share the request/layer metadata and,
+//    within a head group, the B rows, which stay in registers.
+//  * Decay weights come from a wavefront-level suffix-product scan over the k
+//    per-token decays a_j = exp(dt_j A_h) held one per lane.
+//  * w_j * x_j is staged per wavefront in LDS ([row][token], fp32); each lane
+//    owns 8 consecutive columns, keeps B_j for those columns in registers, and
+//    streams its rows of the tile through registers with 16-byte loads (8-byte
+//    for one-byte state), folding k multiply-adds per element.  No MFMA: the
+//    path moves ~4 bytes per 2k+1 flops and is bound by HBM.
+//  * No workgroup barriers: the four waves of a workgroup are independent.
+#pragma once
+
+#include "rssm_device.h"
+
+namespace rssm {
+
+constexpr int kWaves = 4;             // wavefronts per workgroup
+constexpr int kBlock = 64 * kWaves;   // threads per workgroup
+
+struct KernelArgs {
+  const int64_t* state_ptrs;
+  const int64_t* state_strides;
+  const int64_t* x_ptrs;
+  const int64_t* x_strides;
+  const int64_t* B_ptrs;
+  const int64_t* B_strides;
+  const int64_t* dt_ptrs;
+  const int64_t* dt_strides;
+  const int64_t* A_ptrs;
+  const int64_t* scale_ptrs;
+  const int64_t* scale_strides;
+  const int32_t* src_slots;
+  const int32_t* dst_slots;
+  const int32_t* ring_start;
+  const int32_t* prefix_len;
+  const int32_t* active;
+  const int64_t* rand_seed;
+  int32_t L, B, H, hpg, R, W, pad, rounds;
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Orders this wavefront's LDS traffic: the compiler may not move LDS accesses
+// across it, and it waits for outstanding LDS operations.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of requests before the first entry that is -1 (or outside [0, B)).
+__device__ __forceinline__ int count_active(const int32_t* active, int B, int lane) {
+  for (int base = 0; base < B; base += 256) {
+    int v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = base + 64 * q + lane;
+      v[q] = (idx < B) ? active[idx] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t stop = __ballot(v[q] < 0 || v[q] >= B);
+      if (stop) return base + 64 * q + __builtin_ctzll(stop);
+    }
+  }
+  return B;
+}
+
+// Max over the 16 lanes of an aligned lane group (one state row).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  v = fmaxf(v, __shfl_xor(v, 4, 16));
+  v = fmaxf(v, __shfl_xor(v, 2, 16));
+  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  return v;
+}
+
+// Encode this lane's 8 fp32 values of one state row.  One-byte state reduces
+// the row max over the row's 16 lanes (all 64 lanes must execute this) and
+// returns the new row scale in `row_scale`.
+template <int ST, bool SR>
+__device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const uint32_t (&u)[8],
+                                                  float& row_scale) {
+  Chunk<ST> out;
+  if constexpr (ST == kF32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out.w[i] = __float_as_uint(acc[i]);
+  } else if constexpr (ST == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out.w[i] = bf16_round(acc[2 * i], SR, u[2 * i]) | (bf16_round(acc[2 * i + 1], SR, u[2 * i + 1]) << 16);
+  } else if constexpr (ST == kF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out.w[i] = f16_round(acc[2 * i], SR, u[2 * i]) | (f16_round(acc[2 * i + 1], SR, u[2 * i + 1]) << 16);
+  } else {
+    // Per-row symmetric quantization: scale = rowmax/qmax, t = v * (qmax/rowmax),
+    // both IEEE fp32 divisions.  An all-zero row (or one whose inverse
+    // overflows) stores scale 0 and zero codes.
+    constexpr float qmax = (ST == kI8) ? 127.0f : 448.0f;
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(acc[i]));
+    m = row16_max(m);
+    const float inv = qmax / m;
+    const bool ok = (m > 0.0f) && !__builtin_isinf(m) && __builtin_isfinite(inv);
+    row_scale = ok ? m / qmax : 0.0f;
+    uint32_t code[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = acc[i] * inv;
+      const uint32_t c = (ST == kI8) ? i8_round(t, SR, u[i]) : e4m3_round(t, SR, u[i]);
+      code[i] = ok ? c : 0u;
+    }
+    out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+  }
+  return out;
+}
+
+// Address = wave-uniform base + 32-bit per-lane byte offset (the scalar-base
+// addressing mode; keeps per-pass addresses out of vector registers).
+template <typename T>
+__device__ __forceinline__ T* at(T* uniform_base, uint32_t lane_off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(uniform_base) + lane_off);
+}
+
+// Ring entry of token j: (r0 + j) mod R, for 0 <= r0 < R and j < 16.
+__device__ __forceinline__ int ring_entry(int r0, int j, int R) {
+  int e = r0 + j;
+  while (e >= R) e -= R;
+  return e;
+}
+
+// Resident wavefronts per SIMD the register budget is sized for: B_j for 8
+// columns costs 8*KMAX registers per lane.
+template <int KMAX> constexpr int kWavesPerSimd = (KMAX <= 8) ? 4 : 2;
+
+template <int ST, int IT, int DIM, int DSTATE, int KMAX, bool SR>
+__global__ void __launch_bounds__(kBlock, kWavesPerSimd<KMAX>) materialize_kernel(const KernelArgs a) {
+  constexpr int TPR = DSTATE / 8;                 // lanes per state row
+  constexpr int RPP = 64 / TPR;                   // rows per pass of a wavefront
+  constexpr int NPASS = (DIM + RPP - 1) / RPP;    // passes per tile
+  constexpr bool kFull = (NPASS * RPP == DIM);
+  constexpr int SB = Fmt<ST>::bytes;
+  constexpr int IB = Fmt<IT>::bytes;
+  constexpr int CW = 2 * SB;                      // dwords per 8-element chunk
+  constexpr int PD = (NPASS < 16 / CW) ? NPASS : 16 / CW;  // passes in flight (16 dwords/lane)
+  static_assert(NPASS % PD == 0, "passes must split into prefetch groups");
+  constexpr int64_t kTile = static_cast<int64_t>(DIM) * DSTATE;
+  constexpr int XCH = DIM / 8;                    // 8-row chunks of one x row
+  constexpr bool Q = kOneByte<ST>;
+  static_assert(DSTATE % 8 == 0 && 64 % TPR == 0 && DIM % 8 == 0, "unsupported tile shape");
+  static_assert(!Q || TPR == 16, "one-byte state needs 16 lanes per row");
+  static_assert(KMAX % 4 == 0 && KMAX <= 16, "KMAX");
+
+  __shared__ __attribute__((aligned(16))) float lds_wx[kWaves][DIM * KMAX];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
+  float* wx = lds_wx[wave];
+  const int cc = lane % TPR;
+  const int rr = lane / TPR;
+  constexpr int PS = RPP * DSTATE * SB;  // bytes between passes of a tile
+  const uint32_t lane_off = static_cast<uint32_t>((rr * DSTATE + cc * 8) * SB);  // this lane's chunk in a pass
+
+  const int n_active = uniform(count_active(a.active, a.B, lane));
+  const int64_t items = static_cast<int64_t>(n_active) * a.L * a.H;
+  if (items == 0) return;
+
+  // Contiguous, balanced item range of this wavefront.
+  const int64_t tw = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t per = items / tw, rem = items % tw;
+  int64_t it = gw * per + (gw < rem ? gw : rem);
+  const int64_t end = it + per + (gw < rem ? 1 : 0);
+
+  uint32_t key0 = 0, key1 = 0;
+  if constexpr (SR) {
+    const uint64_t sd = static_cast<uint64_t>(*a.rand_seed);
+    key0 = static_cast<uint32_t>(uniform(static_cast<int>(sd & 0xFFFFFFFFu)));
+    key1 = static_cast<uint32_t>(uniform(static_cast<int>(sd >> 32)));
+  }
+  const int G = a.H / a.hpg;
+
+  while (it < end) {
+    // One (request, layer): heads [h0, h1) of it belong to this wavefront.
+    const int64_t il = it / a.H;
+    const int h0 = static_cast<int>(it - il * a.H);
+    const int h1 = static_cast<int>(min(static_cast<int64_t>(a.H), h0 + (end - it)));
+    it += h1 - h0;
+
+    const int i = static_cast<int>(il / a.L);
+    const int l = static_cast<int>(il - static_cast<int64_t>(i) * a.L);
+    const int b = uniform(a.active[i]);
+    const int64_t lb = static_cast<int64_t>(l) * a.B + b;
+    const int s = uniform(a.src_slots[lb]);
+    const int d = uniform(a.dst_slots[lb]);
+    if (s == a.pad || d == a.pad || s < 0 || d < 0) continue;  // pad slot: skipped
+    const int k = min(max(uniform(a.prefix_len[b]), 0), a.W);
+    int r0 = uniform(a.ring_start[b]) % a.R;
+    if (r0 < 0) r0 += a.R;
+
+    const int64_t sbase = uniform64(a.state_ptrs[l]);
+    const int64_t sstride = uniform64(a.state_strides[l]);
+    const char* src_state = reinterpret_cast<const char*>(sbase) + static_cast<int64_t>(s) * sstride * SB;
+    char* dst_state = reinterpret_cast<char*>(sbase) + static_cast<int64_t>(d) * sstride * SB;
+    const float* src_scale = nullptr;
+    float* dst_scale = nullptr;
+    if constexpr (Q) {
+      const int64_t cbase = uniform64(a.scale_ptrs[l]);
+      const int64_t cstride = uniform64(a.scale_strides[l]);
+      src_scale = reinterpret_cast<const float*>(cbase) + static_cast<int64_t>(s) * cstride;
+      dst_scale = reinterpret_cast<float*>(cbase) + static_cast<int64_t>(d) * cstride;
+    }
+
+    if (k == 0) {
+      // Zero prefix: exact byte copy of each tile (and its row scales).
+      for (int h = h0; h < h1; ++h) {
+        const char* src_tile = src_state + h * kTile * SB;
+        char* dst_tile = dst_state + h * kTile * SB;
+#pragma unroll 1
+        for (int p0 = 0; p0 < NPASS; p0 += PD) {
+          Chunk<ST> c[PD];
+#pragma unroll
+          for (int q = 0; q < PD; ++q) {
+            const int r = rr + (p0 + q) * RPP;
+            if (kFull || r < DIM) c[q] = load_chunk<ST>(at(src_tile + (p0 + q) * PS, lane_off));
+          }
+#pragma unroll
+          for (int q = 0; q < PD; ++q) {
+            const int r = rr + (p0 + q) * RPP;
+            if (kFull || r < DIM) {
+              store_chunk<ST>(at(dst_tile + (p0 + q) * PS, lane_off), c[q]);
+              if constexpr (Q) {
+                if (cc == 0) dst_scale[h * DIM + r] = src_scale[h * DIM + r];
+              }
+            }
+          }
+        }
+      }
+      continue;
+    }
+
+    const char* x_slot = reinterpret_cast<const char*>(uniform64(a.x_ptrs[l])) +
+                         static_cast<int64_t>(s) * uniform64(a.x_strides[l]) * IB;
+    const char* B_slot = reinterpret_cast<const char*>(uniform64(a.B_ptrs[l])) +
+                         static_cast<int64_t>(s) * uniform64(a.B_strides[l]) * IB;
+    const float* dt_slot = reinterpret_cast<const float*>(uniform64(a.dt_ptrs[l])) +
+                           static_cast<int64_t>(s) * uniform64(a.dt_strides[l]);
+    const float* A = reinterpret_cast<const float*>(uniform64(a.A_ptrs[l]));
+    const int e_lane = (r0 + lane) % a.R;  // ring entry of token `lane`
+
+    for (int g = h0 / a.hpg; g * a.hpg < h1; ++g) {
+      // B_j for this lane's 8 columns, shared by the heads of group g.
+      float Bv[KMAX][8];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          const int e = ring_entry(r0, j, a.R);
+          const Chunk<IT> c = load_chunk<IT>(B_slot + ((static_cast<int64_t>(e) * G + g) * DSTATE + cc * 8) * IB);
+          decode_chunk<IT>(c, Bv[j]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) Bv[j][q] = 0.0f;
+        }
+      }
+      const int hb = max(h0, g * a.hpg);
+      const int he = min(h1, (g + 1) * a.hpg);
+      for (int h = hb; h < he; ++h) {
+        const char* src_tile = src_state + h * kTile * SB;
+        char* dst_tile = dst_state + h * kTile * SB;
+        const float* src_sc = Q ? src_scale + static_cast<int64_t>(h) * DIM : nullptr;
+        float* dst_sc = Q ? dst_scale + static_cast<int64_t>(h) * DIM : nullptr;
+
+        // Issue the first passes of the state stream before the ring work.
+        Chunk<ST> buf[PD];
+        float sbuf[PD];
+#pragma unroll
+        for (int p = 0; p < PD; ++p) {
+          const int r = rr + p * RPP;
+          if (kFull || r < DIM) {
+            buf[p] = load_chunk<ST>(at(src_tile + p * PS, lane_off));
+            if constexpr (Q) sbuf[p] = src_sc[r];
+          }
+        }
+
+        // Decay scan: lane j < k holds a_j; suffix products give D and w_j.
+        const float A_h = A[h];
+        float dtj = 0.0f, aj = 1.0f;
+        if (lane < k) {
+          dtj = dt_slot[static_cast<int64_t>(e_lane) * a.H + h];
+          aj = expf(dtj * A_h);
+        }
+        float P = aj;  // inclusive suffix product over lanes j..15
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float o = __shfl_down(P, off);
+          if (lane + off < 16) P *= o;
+        }
+        float Pn = __shfl_down(P, 1);
+        if (lane >= 15) Pn = 1.0f;
+        const float w = dtj * Pn;
+        const float D = __shfl(P, 0);
+
+        // Stage w_j * x_j[r] into this wave's LDS as [row][token]; tokens
+        // k..ceil4(k)-1 are written as zero.
+        const int k4 = (k + 3) & ~3;
+        wave_lds_fence();
+#pragma unroll
+        for (int rep = 0; rep < (KMAX * XCH + 63) / 64; ++rep) {
+          const int idx = lane + 64 * rep;
+          const int j = min(idx / XCH, 63);
+          const float wj = __shfl(w, j);
+          const int ej = __shfl(e_lane, j);
+          if (idx < k4 * XCH) {
+            const int r8 = (idx % XCH) * 8;
+            float xv[8];
+            if (j < k) {
+              const Chunk<IT> c = load_chunk<IT>(x_slot + ((static_cast<int64_t>(ej) * a.H + h) * DIM + r8) * IB);
+              decode_chunk<IT>(c, xv);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) xv[q] = 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) wx[(r8 + q) * KMAX + j] = wj * xv[q];
+          }
+        }
+        wave_lds_fence();
+
+        // Stream the tile: decode, fold the prefix, encode, store.  Passes go
+        // in groups of PD; while a group is folded the next group is in flight.
+#pragma unroll 1
+        for (int p0 = 0; p0 < NPASS; p0 += PD) {
+#pragma unroll
+          for (int q = 0; q < PD; ++q) {
+            const int p = p0 + q;
+            const Chunk<ST> cur = buf[q];
+            const float cur_sc = Q ? sbuf[q] : 1.0f;
+            if (p + PD < NPASS) {
+              const int rn = rr + (p + PD) * RPP;
+              if (kFull || rn < DIM) {
+                buf[q] = load_chunk<ST>(at(src_tile + (p + PD) * PS, lane_off));
+                if constexpr (Q) sbuf[q] = src_sc[rn];
+              }
+            }
+            const int r = rr + p * RPP;
+            if (kFull || r < DIM) {
+              float acc[8];
+              decode_chunk<ST>(cur, acc);
+              const float d0 = Q ? cur_sc * D : D;
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[c] *= d0;
+              const float* wrow = wx + r * KMAX;
+#pragma unroll
+              for (int jb = 0; jb < KMAX / 4; ++jb) {
+                if (jb * 4 < k) {
+                  const float4 w4 = *reinterpret_cast<const float4*>(wrow + jb * 4);
+#pragma unroll
+                  for (int c = 0; c < 8; ++c) {
+                    acc[c] = fmaf(w4.x, Bv[jb * 4 + 0][c], acc[c]);
+                    acc[c] = fmaf(w4.y, Bv[jb * 4 + 1][c], acc[c]);
+                    acc[c] = fmaf(w4.z, Bv[jb * 4 + 2][c], acc[c]);
+                    acc[c] = fmaf(w4.w, Bv[jb * 4 + 3][c], acc[c]);
+                  }
+                }
+              }
+              uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+              if constexpr (SR) sr_words(u, r, cc * 8, DSTATE, h, b, l, key0, key1, a.rounds);
+              float rs = 0.0f;
+              const Chunk<ST> out = encode_chunk<ST, SR>(acc, u, rs);
+              store_chunk<ST>(at(dst_tile + p * PS, lane_off), out);
+              if constexpr (Q) {
+                if (cc == 0) dst_sc[r] = rs;
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Test hook: the same encode step on caller-given fp32 rows.
+template <int ST, int DSTATE, bool SR>
+__global__ void __launch_bounds__(kBlock) encode_rows_kernel(const float* rows, const int32_t* coords,
+                                                            const int64_t* rand_seed, char* out_codes,
+                                                            float* out_scales, int n, int rounds) {
+  constexpr int TPR = DSTATE / 8;
+  constexpr int RPW = 64 / TPR;
+  constexpr int SB = Fmt<ST>::bytes;
+  const int lane = threadIdx.x & 63;
+  const int64_t gwave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t row = gwave * RPW + lane / TPR;
+  const int cc = lane % TPR;
+  const bool ok = row < n;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = ok ? rows[row * DSTATE + cc * 8 + q] : 0.0f;
+  uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  if constexpr (SR) {
+    const uint64_t s = static_cast<uint64_t>(*rand_seed);
+    const int l = ok ? coords[row * 4 + 0] : 0;
+    const int b = ok ? coords[row * 4 + 1] : 0;
+    const int h = ok ? coords[row * 4 + 2] : 0;
+    const int r = ok ? coords[row * 4 + 3] : 0;
+    sr_words(u, r, cc * 8, DSTATE, h, b, l, static_cast<uint32_t>(s), static_cast<uint32_t>(s >> 32), rounds);
+  }
+  float rs = 0.0f;
+  const Chunk<ST> c = encode_chunk<ST, SR>(acc, u, rs);
+  if (ok) {
+    store_chunk<ST>(out_codes + (row * DSTATE + cc * 8) * SB, c);
+    if constexpr (kOneByte<ST>) {
+      if (cc == 0) out_scales[row] = rs;
+    }
+  }
+}
+
+// Kernel registry entries, one table per state dtype (one translation unit each).
+struct KernelEntry {
+  int st, it, dim, dstate, kmax, sr;
+  const void* fn;
+  const char* name;
+};
+
+struct EncodeEntry {
+  int st, dstate, sr;
+  const void* fn;
+  const char* name;
+};
+
+}  // namespace rssm

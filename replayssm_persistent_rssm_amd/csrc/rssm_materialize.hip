@@ -1,0 +1,351 @@
+// rssm_materialize.hip -- host side of librssm_materialize: validation of the
+// host-visible arguments, instance selection, persistent-grid sizing and the
+// launch on the caller's stream.  The C ABI is declared in rssm_materialize.h.
+//
+// Host validation mirrors the parameter rules of the flashinfer page for
+// flashinfer.mamba.replayssm_materialize (heads_per_group divides num_heads;
+// max_window in [1, 16]; one-byte state needs dim 64 and dstate 128; a seed
+// when philox_rounds > 0) and the pull-request review's point that the head
+// count must never be narrowed (here it is int32 by type, and the work size
+// L*B*H is bounded so that the kernel's 64-bit item arithmetic cannot
+// overflow).  Device metadata is never read on the host.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "rssm_kernel.h"
+#include "rssm_materialize.h"
+
+namespace rssm {
+const KernelEntry* kernels_f32(int* n);
+const KernelEntry* kernels_bf16(int* n);
+const KernelEntry* kernels_f16(int* n);
+const KernelEntry* kernels_i8(int* n);
+const KernelEntry* kernels_f8(int* n);
+const EncodeEntry* encoders_f32(int* n);
+const EncodeEntry* encoders_bf16(int* n);
+const EncodeEntry* encoders_f16(int* n);
+const EncodeEntry* encoders_i8(int* n);
+const EncodeEntry* encoders_f8(int* n);
+}  // namespace rssm
+
+namespace {
+
+thread_local char g_err[1024];
+
+rssm_status fail(rssm_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool verbose() {
+  static const bool v = [] {
+    const char* e = std::getenv("RSSM_MATERIALIZE_VERBOSE");
+    return e != nullptr && *e != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  return v;
+}
+
+const char* dtype_name(int d) {
+  switch (d) {
+    case RSSM_F32: return "f32";
+    case RSSM_BF16: return "bf16";
+    case RSSM_F16: return "f16";
+    case RSSM_I8: return "i8";
+    case RSSM_F8E4M3: return "f8e4m3";
+    default: return "?";
+  }
+}
+
+bool one_byte(int d) { return d == RSSM_I8 || d == RSSM_F8E4M3; }
+
+template <typename T>
+bool aligned(const T* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Compiled (dim, dstate) shapes.
+bool shape_supported(int state_dtype, int dim, int dstate) {
+  if (dim == 64 && dstate == 128) return true;
+  return !one_byte(state_dtype) && dim == 16 && dstate == 16;
+}
+
+rssm_status validate_desc(const rssm_materialize_desc* d) {
+  if (d == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->num_layers < 1) return fail(RSSM_ERR_INVALID_ARGUMENT, "num_layers must be >= 1 (got %d)", d->num_layers);
+  if (d->batch < 1) return fail(RSSM_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", d->batch);
+  if (d->num_heads < 1) return fail(RSSM_ERR_INVALID_ARGUMENT, "num_heads must be >= 1 (got %d)", d->num_heads);
+  if (d->heads_per_group < 1 || d->num_heads % d->heads_per_group != 0)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "heads_per_group (%d) must be >= 1 and divide num_heads (%d)",
+                d->heads_per_group, d->num_heads);
+  if (d->dim < 1 || d->dstate < 1)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "dim and dstate must be >= 1 (got %d, %d)", d->dim, d->dstate);
+  if (d->max_window < 1 || d->max_window > 16)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "max_window must be in [1, 16] (got %d)", d->max_window);
+  if (d->ring_buffer_len < 1)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "ring_buffer_len must be >= 1 (got %d)", d->ring_buffer_len);
+  if (d->philox_rounds < 0 || d->philox_rounds > 64)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "philox_rounds must be in [0, 64] (got %d)", d->philox_rounds);
+  if (d->max_workgroups < 0)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "max_workgroups must be >= 0 (got %d)", d->max_workgroups);
+  if (d->state_dtype < RSSM_F32 || d->state_dtype > RSSM_F8E4M3)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "unknown state_dtype %d", d->state_dtype);
+  if (d->input_dtype < RSSM_F32 || d->input_dtype > RSSM_F8E4M3)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "unknown input_dtype %d", d->input_dtype);
+  if (d->a_dtype < RSSM_F32 || d->a_dtype > RSSM_F8E4M3)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "unknown a_dtype %d", d->a_dtype);
+  if (d->input_dtype != RSSM_F32 && d->input_dtype != RSSM_BF16 && d->input_dtype != RSSM_F16)
+    return fail(RSSM_ERR_UNSUPPORTED, "input_dtype %s is not supported (f32, bf16, f16)", dtype_name(d->input_dtype));
+  if (d->a_dtype != RSSM_F32)
+    return fail(RSSM_ERR_UNSUPPORTED, "a_dtype %s is not supported (f32)", dtype_name(d->a_dtype));
+  if (one_byte(d->state_dtype) && (d->dim != 64 || d->dstate != 128))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "one-byte state requires dim=64 and dstate=128 (got %d, %d)", d->dim,
+                d->dstate);
+  if (!shape_supported(d->state_dtype, d->dim, d->dstate))
+    return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance for dim=%d dstate=%d with %s state", d->dim, d->dstate,
+                dtype_name(d->state_dtype));
+  const int64_t work = static_cast<int64_t>(d->num_layers) * d->batch * d->num_heads;
+  if (work > (int64_t(1) << 40))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "num_layers*batch*num_heads = %lld exceeds 2^40",
+                static_cast<long long>(work));
+  return RSSM_OK;
+}
+
+rssm_status validate_tables(const rssm_materialize_desc* d, const rssm_materialize_tables* t) {
+  if (t == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "tables is NULL");
+  struct P64 { const int64_t* p; const char* n; } p64[] = {
+      {t->state_ptrs, "state_ptrs"}, {t->state_slot_strides, "state_slot_strides"},
+      {t->x_ptrs, "x_ptrs"}, {t->x_slot_strides, "x_slot_strides"},
+      {t->B_ptrs, "B_ptrs"}, {t->B_slot_strides, "B_slot_strides"},
+      {t->dt_ptrs, "dt_ptrs"}, {t->dt_slot_strides, "dt_slot_strides"},
+      {t->A_ptrs, "A_ptrs"}};
+  for (const auto& e : p64) {
+    if (e.p == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is NULL", e.n);
+    if (!aligned(e.p, 8)) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is not 8-byte aligned", e.n);
+  }
+  struct P32 { const int32_t* p; const char* n; } p32[] = {
+      {t->src_slots, "src_slots"}, {t->dst_slots, "dst_slots"}, {t->ring_start, "ring_start"},
+      {t->replay_prefix_len, "replay_prefix_len"}, {t->active_request_indices, "active_request_indices"}};
+  for (const auto& e : p32) {
+    if (e.p == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is NULL", e.n);
+    if (!aligned(e.p, 4)) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", e.n);
+  }
+  if (one_byte(d->state_dtype)) {
+    if (t->scale_ptrs == nullptr || t->scale_slot_strides == nullptr)
+      return fail(RSSM_ERR_INVALID_ARGUMENT, "one-byte state needs scale_ptrs and scale_slot_strides");
+    if (!aligned(t->scale_ptrs, 8) || !aligned(t->scale_slot_strides, 8))
+      return fail(RSSM_ERR_INVALID_ARGUMENT, "scale tables are not 8-byte aligned");
+  }
+  if (d->philox_rounds > 0) {
+    if (t->rand_seed == nullptr)
+      return fail(RSSM_ERR_INVALID_ARGUMENT, "rand_seed is required when philox_rounds > 0");
+    if (!aligned(t->rand_seed, 8)) return fail(RSSM_ERR_INVALID_ARGUMENT, "rand_seed is not 8-byte aligned");
+  }
+  return RSSM_OK;
+}
+
+struct Registry {
+  const rssm::KernelEntry* k[5];
+  int nk[5];
+  const rssm::EncodeEntry* e[5];
+  int ne[5];
+  Registry() {
+    k[0] = rssm::kernels_f32(&nk[0]);
+    k[1] = rssm::kernels_bf16(&nk[1]);
+    k[2] = rssm::kernels_f16(&nk[2]);
+    k[3] = rssm::kernels_i8(&nk[3]);
+    k[4] = rssm::kernels_f8(&nk[4]);
+    e[0] = rssm::encoders_f32(&ne[0]);
+    e[1] = rssm::encoders_bf16(&ne[1]);
+    e[2] = rssm::encoders_f16(&ne[2]);
+    e[3] = rssm::encoders_i8(&ne[3]);
+    e[4] = rssm::encoders_f8(&ne[4]);
+  }
+};
+
+const Registry& registry() {
+  static const Registry r;
+  return r;
+}
+
+const rssm::KernelEntry* find_kernel(const rssm_materialize_desc* d) {
+  const int kmax = d->max_window <= 8 ? 8 : 16;
+  const int sr = (d->philox_rounds > 0 && d->state_dtype != RSSM_F32) ? 1 : 0;
+  const Registry& reg = registry();
+  const int s = d->state_dtype;
+  for (int i = 0; i < reg.nk[s]; ++i) {
+    const rssm::KernelEntry& e = reg.k[s][i];
+    if (e.it == d->input_dtype && e.dim == d->dim && e.dstate == d->dstate && e.kmax == kmax && e.sr == sr)
+      return &e;
+  }
+  return nullptr;
+}
+
+const rssm::EncodeEntry* find_encoder(const rssm_materialize_desc* d) {
+  const int sr = (d->philox_rounds > 0 && d->state_dtype != RSSM_F32) ? 1 : 0;
+  const Registry& reg = registry();
+  const int s = d->state_dtype;
+  for (int i = 0; i < reg.ne[s]; ++i) {
+    const rssm::EncodeEntry& e = reg.e[s][i];
+    if (e.dstate == d->dstate && e.sr == sr) return &e;
+  }
+  return nullptr;
+}
+
+// Cached device properties and per-kernel occupancy.
+std::mutex g_mu;
+std::unordered_map<int, int> g_cus;                      // device -> compute units
+std::unordered_map<const void*, int> g_occ;              // kernel -> resident workgroups per CU
+
+rssm_status grid_for(const void* fn, int* grid_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RSSM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(RSSM_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    it = g_cus.emplace(dev, cus).first;
+  }
+  auto ot = g_occ.find(fn);
+  if (ot == g_occ.end()) {
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, rssm::kBlock, 0);
+    if (e != hipSuccess) return fail(RSSM_ERR_HIP, "hipOccupancyMaxActiveBlocksPerMultiprocessor: %s",
+                                     hipGetErrorString(e));
+    ot = g_occ.emplace(fn, nb < 1 ? 1 : nb).first;
+  }
+  *grid_out = it->second * ot->second;
+  return RSSM_OK;
+}
+
+int lds_bytes_of(const rssm_materialize_desc* d) {
+  const int kmax = d->max_window <= 8 ? 8 : 16;
+  return rssm::kWaves * d->dim * kmax * static_cast<int>(sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rssm_last_error(void) { return g_err; }
+
+rssm_status rssm_materialize_launch_config(const rssm_materialize_desc* desc, int32_t* grid, int32_t* block,
+                                           int32_t* lds_bytes) {
+  g_err[0] = '\0';
+  rssm_status st = validate_desc(desc);
+  if (st != RSSM_OK) return st;
+  if (grid == nullptr || block == nullptr || lds_bytes == nullptr)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "grid, block and lds_bytes must not be NULL");
+  const rssm::KernelEntry* k = find_kernel(desc);
+  if (k == nullptr) return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance");
+  int g = 0;
+  if (desc->max_workgroups > 0) {
+    g = desc->max_workgroups;
+  } else {
+    st = grid_for(k->fn, &g);
+    if (st != RSSM_OK) return st;
+  }
+  *grid = g;
+  *block = rssm::kBlock;
+  *lds_bytes = lds_bytes_of(desc);
+  return RSSM_OK;
+}
+
+rssm_status rssm_materialize(const rssm_materialize_desc* desc, const rssm_materialize_tables* tables,
+                             void* hip_stream) {
+  g_err[0] = '\0';
+  rssm_status st = validate_desc(desc);
+  if (st != RSSM_OK) return st;
+  st = validate_tables(desc, tables);
+  if (st != RSSM_OK) return st;
+  const rssm::KernelEntry* k = find_kernel(desc);
+  if (k == nullptr)
+    return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance for state=%s input=%s dim=%d dstate=%d",
+                dtype_name(desc->state_dtype), dtype_name(desc->input_dtype), desc->dim, desc->dstate);
+  int grid = desc->max_workgroups;
+  if (grid == 0) {
+    st = grid_for(k->fn, &grid);
+    if (st != RSSM_OK) return st;
+  }
+  rssm::KernelArgs args;
+  args.state_ptrs = tables->state_ptrs;
+  args.state_strides = tables->state_slot_strides;
+  args.x_ptrs = tables->x_ptrs;
+  args.x_strides = tables->x_slot_strides;
+  args.B_ptrs = tables->B_ptrs;
+  args.B_strides = tables->B_slot_strides;
+  args.dt_ptrs = tables->dt_ptrs;
+  args.dt_strides = tables->dt_slot_strides;
+  args.A_ptrs = tables->A_ptrs;
+  args.scale_ptrs = tables->scale_ptrs;
+  args.scale_strides = tables->scale_slot_strides;
+  args.src_slots = tables->src_slots;
+  args.dst_slots = tables->dst_slots;
+  args.ring_start = tables->ring_start;
+  args.prefix_len = tables->replay_prefix_len;
+  args.active = tables->active_request_indices;
+  args.rand_seed = tables->rand_seed;
+  args.L = desc->num_layers;
+  args.B = desc->batch;
+  args.H = desc->num_heads;
+  args.hpg = desc->heads_per_group;
+  args.R = desc->ring_buffer_len;
+  args.W = desc->max_window;
+  args.pad = desc->pad_slot_id;
+  args.rounds = desc->philox_rounds;
+  if (verbose())
+    std::fprintf(stderr, "[rssm_materialize] %s grid=%d block=%d lds=%dB L=%d B=%d H=%d\n", k->name, grid,
+                 rssm::kBlock, lds_bytes_of(desc), desc->num_layers, desc->batch, desc->num_heads);
+  void* params[] = {&args};
+  hipError_t e = hipLaunchKernel(k->fn, dim3(grid), dim3(rssm::kBlock), params, 0,
+                                 static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(RSSM_ERR_HIP, "launch of %s failed: %s", k->name, hipGetErrorString(e));
+  return RSSM_OK;
+}
+
+rssm_status rssm_debug_encode_rows(const rssm_materialize_desc* desc, const float* rows, const int32_t* coords,
+                                   const int64_t* rand_seed, void* out_codes, float* out_scales, int32_t n,
+                                   void* hip_stream) {
+  g_err[0] = '\0';
+  if (desc == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (desc->state_dtype < RSSM_F32 || desc->state_dtype > RSSM_F8E4M3)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "unknown state_dtype %d", desc->state_dtype);
+  if (desc->philox_rounds < 0 || desc->philox_rounds > 64)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "philox_rounds must be in [0, 64]");
+  if (n < 0) return fail(RSSM_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  const bool ob = one_byte(desc->state_dtype);
+  if (!(desc->dstate == 128 || (!ob && desc->dstate == 16)))
+    return fail(RSSM_ERR_UNSUPPORTED, "dstate %d not supported for %s rows", desc->dstate,
+                dtype_name(desc->state_dtype));
+  if (n == 0) return RSSM_OK;
+  if (rows == nullptr || out_codes == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "rows/out_codes NULL");
+  if (ob && out_scales == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "out_scales NULL for one-byte state");
+  if (desc->philox_rounds > 0 && (rand_seed == nullptr || coords == nullptr))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "rand_seed and coords are required when philox_rounds > 0");
+  const rssm::EncodeEntry* e = find_encoder(desc);
+  if (e == nullptr) return fail(RSSM_ERR_UNSUPPORTED, "no compiled encode instance");
+  const int rows_per_block = rssm::kWaves * (64 / (desc->dstate / 8));
+  const int grid = static_cast<int>((static_cast<int64_t>(n) + rows_per_block - 1) / rows_per_block);
+  int rounds = desc->philox_rounds;
+  char* codes = static_cast<char*>(out_codes);
+  void* params[] = {&rows, &coords, &rand_seed, &codes, &out_scales, &n, &rounds};
+  hipError_t err = hipLaunchKernel(e->fn, dim3(grid), dim3(rssm::kBlock), params, 0,
+                                   static_cast<hipStream_t>(hip_stream));
+  if (err != hipSuccess) return fail(RSSM_ERR_HIP, "launch of %s failed: %s", e->name, hipGetErrorString(err));
+  return RSSM_OK;
+}
+
+}  // extern "C"

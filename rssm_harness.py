@@ -1,0 +1,127 @@
+"""Drive librssm_materialize on the seeded workloads of ``rssm_inputs``.
+
+Marshalling only: upload host problems to the device, build the per-layer
+pointer/stride tables and metadata tensors, call the library through its
+binding, download results.  Used by the GPU tests, the smoke check and the
+benchmark.  It never imports the CPU oracle.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+import rssm_inputs as ri
+
+
+def _np_to_dev(a: np.ndarray, device):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def upload(prob: ri.Problem, device="cuda") -> ri.DeviceProblem:
+    """Copy a host problem to the device with the same per-layer layout."""
+    up = lambda arrs: [_np_to_dev(x, device) for x in arrs] if arrs is not None else None  # noqa: E731
+    return ri.DeviceProblem(spec=prob.spec, meta=prob.meta, state=up(prob.state), scale=up(prob.scale),
+                            x=up(prob.x), Bm=up(prob.Bm), dt=up(prob.dt), A=up(prob.A))
+
+
+def download(tensors, like: Optional[list] = None):
+    out = []
+    for i, t in enumerate(tensors):
+        a = t.detach().cpu().contiguous()
+        import torch
+        if a.dtype == torch.bfloat16:
+            a = a.view(torch.int16)
+        n = a.numpy()
+        if like is not None:
+            n = n.view(like[i].dtype)
+        elif n.dtype == np.int16:
+            n = n.view(np.uint16)
+        out.append(n)
+    return out
+
+
+@dataclasses.dataclass
+class Tables:
+    state_ptrs: object
+    state_slot_strides: object
+    x_cache_ptrs: object
+    x_cache_slot_strides: object
+    B_cache_ptrs: object
+    B_cache_slot_strides: object
+    dt_cache_ptrs: object
+    dt_cache_slot_strides: object
+    A_ptrs: object
+    state_scale_ptrs: object
+    state_scale_slot_strides: object
+    src_slots: object
+    dst_slots: object
+    ring_start: object
+    replay_prefix_len: object
+    active_request_indices: object
+    rand_seed: object
+
+
+def tables(dp: ri.DeviceProblem, device="cuda", active: Optional[np.ndarray] = None) -> Tables:
+    import torch
+    from replayssm_persistent_rssm_amd import pointer_table, stride_table
+    m = dp.meta
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)  # noqa: E731
+    seed = dp.spec.rand_seed
+    return Tables(
+        state_ptrs=pointer_table(dp.state, device), state_slot_strides=stride_table(m.state_stride, device),
+        x_cache_ptrs=pointer_table(dp.x, device), x_cache_slot_strides=stride_table(m.x_stride, device),
+        B_cache_ptrs=pointer_table(dp.Bm, device), B_cache_slot_strides=stride_table(m.B_stride, device),
+        dt_cache_ptrs=pointer_table(dp.dt, device), dt_cache_slot_strides=stride_table(m.dt_stride, device),
+        A_ptrs=pointer_table(dp.A, device),
+        state_scale_ptrs=pointer_table(dp.scale, device) if dp.scale else None,
+        state_scale_slot_strides=stride_table(m.scale_stride, device) if dp.scale else None,
+        src_slots=i32(m.src), dst_slots=i32(m.dst), ring_start=i32(m.ring_start),
+        replay_prefix_len=i32(m.prefix), active_request_indices=i32(m.active if active is None else active),
+        rand_seed=torch.tensor([seed if seed is not None else 0], dtype=torch.int64, device=device)
+        if dp.spec.philox_rounds > 0 else None)
+
+
+def materialize(dp: ri.DeviceProblem, tabs: Tables, max_workgroups: int = 0, stream=None,
+                active=None) -> None:
+    """One library call on a device problem (enqueue only)."""
+    from replayssm_persistent_rssm_amd import rssm_materialize
+    s = dp.spec
+    rssm_materialize(
+        tabs.state_ptrs, tabs.state_slot_strides, tabs.x_cache_ptrs, tabs.x_cache_slot_strides,
+        tabs.B_cache_ptrs, tabs.B_cache_slot_strides, tabs.dt_cache_ptrs, tabs.dt_cache_slot_strides,
+        tabs.A_ptrs, tabs.state_scale_ptrs, tabs.state_scale_slot_strides, tabs.src_slots, tabs.dst_slots,
+        tabs.ring_start, tabs.replay_prefix_len,
+        tabs.active_request_indices if active is None else active,
+        state_dtype=s.state_dtype, input_dtype=s.input_dtype, matrixA_dtype="f32", dim=s.dim, dstate=s.dstate,
+        num_heads=s.H, heads_per_group=s.hpg, max_window=s.W, ring_buffer_len=s.R, pad_slot_id=s.pad_slot_id,
+        rand_seed=tabs.rand_seed, philox_rounds=s.philox_rounds, max_workgroups=max_workgroups, stream=stream)
+
+
+def algorithmic_bytes(spec: ri.Spec, meta: ri.Meta, n_active: Optional[int] = None) -> int:
+    """Bytes the method itself must move for one call: per written (layer,
+    request) the state in and out (+ row scales for one-byte state) and, for
+    k > 0, the k replayed x, B and dt rows; plus A per layer touched."""
+    sb = ri.ELEM_BYTES[spec.state_dtype]
+    ib = ri.ELEM_BYTES[spec.input_dtype]
+    total = 0
+    layers = set()
+    n = int((meta.active >= 0).cumprod().sum()) if n_active is None else n_active
+    for i in range(n):
+        b = int(meta.active[i])
+        k = int(meta.prefix[b])
+        for l in range(spec.L):
+            s, d = meta.src[l, b], meta.dst[l, b]
+            if s == spec.pad_slot_id or d == spec.pad_slot_id:
+                continue
+            layers.add(l)
+            total += 2 * spec.H * spec.dim * spec.dstate * sb
+            if ri.one_byte(spec.state_dtype):
+                total += 2 * spec.H * spec.dim * 4
+            total += k * (spec.H * spec.dim * ib + spec.G * spec.dstate * ib + spec.H * 4)
+    return total + len(layers) * spec.H * 4

@@ -1,0 +1,139 @@
+"""The C-ABI library: it loads, exports every entry point its header
+declares, and rejects bad host-visible arguments before any HIP call (so
+these checks run without a GPU).  No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rssm_materialize.h")
+
+
+@pytest.fixture(scope="module")
+def rp():
+    import replayssm_persistent_rssm_amd as rp
+    return rp
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rssm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point(rp):
+    names = declared_functions()
+    assert names == sorted(rp.EXPORTS)
+    for n in names:
+        assert hasattr(rp.lib(), n), n
+
+
+def _desc(rp, **kw):
+    base = dict(num_layers=48, batch=256, num_heads=256, heads_per_group=32, dim=64, dstate=128, max_window=8,
+                ring_buffer_len=16, state_dtype="bf16", input_dtype="bf16")
+    base.update(kw)
+    return rp.make_desc(**base)
+
+
+def _fake_tables(rp, **override):
+    # Aligned, non-NULL addresses that are never dereferenced: every call below
+    # fails host validation before touching the device.
+    t = rp.RssmTables(**{f: 0x10000 for f, _ in rp.RssmTables._fields_})
+    for k, v in override.items():
+        setattr(t, k, v)
+    return t
+
+
+BAD_DESCS = [
+    (dict(num_layers=0), 1, "num_layers"),
+    (dict(batch=0), 1, "batch"),
+    (dict(num_heads=0), 1, "num_heads"),
+    (dict(heads_per_group=3), 1, "divide"),
+    (dict(max_window=0), 1, "max_window"),
+    (dict(max_window=17), 1, "max_window"),
+    (dict(ring_buffer_len=0), 1, "ring_buffer_len"),
+    (dict(philox_rounds=-1), 1, "philox_rounds"),
+    (dict(max_workgroups=-1), 1, "max_workgroups"),
+    (dict(state_dtype=9), 1, "state_dtype"),
+    (dict(input_dtype="i8"), 2, "input_dtype"),
+    (dict(matrixA_dtype="bf16"), 2, "a_dtype"),
+    (dict(state_dtype="i8", dim=32), 1, "one-byte"),
+    (dict(dim=32, dstate=64), 2, "no compiled instance"),
+    (dict(num_layers=2**20, batch=2**20, num_heads=2**10), 1, "2^40"),
+]
+
+
+@pytest.mark.parametrize("kw,status,text", BAD_DESCS)
+def test_bad_scalars_rejected(rp, kw, status, text):
+    d = _desc(rp, **kw)
+    t = _fake_tables(rp)
+    st = rp.lib().rssm_materialize(ctypes.byref(d), ctypes.byref(t), None)
+    assert st == status
+    assert text in rp.rssm_last_error()
+
+
+def test_null_and_misaligned_tables_rejected(rp):
+    d = _desc(rp)
+    assert rp.lib().rssm_materialize(ctypes.byref(d), None, None) == 1
+    assert rp.lib().rssm_materialize(None, None, None) == 1
+    for field in ("state_ptrs", "dt_slot_strides", "A_ptrs", "src_slots", "active_request_indices"):
+        t = _fake_tables(rp, **{field: None})
+        assert rp.lib().rssm_materialize(ctypes.byref(d), ctypes.byref(t), None) == 1
+        assert field in rp.rssm_last_error()
+    t = _fake_tables(rp, state_ptrs=0x10004)
+    assert rp.lib().rssm_materialize(ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert "aligned" in rp.rssm_last_error()
+    t = _fake_tables(rp, ring_start=0x10002)
+    assert rp.lib().rssm_materialize(ctypes.byref(d), ctypes.byref(t), None) == 1
+
+
+def test_quantized_state_needs_scales_and_sr_needs_seed(rp):
+    d = _desc(rp, state_dtype="f8e4m3")
+    t = _fake_tables(rp, scale_ptrs=None)
+    assert rp.lib().rssm_materialize(ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert "scale" in rp.rssm_last_error()
+    d = _desc(rp, state_dtype="bf16", philox_rounds=10)
+    t = _fake_tables(rp, rand_seed=None)
+    assert rp.lib().rssm_materialize(ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert "rand_seed" in rp.rssm_last_error()
+
+
+def test_python_binding_rejects_out_of_range_scalars(rp):
+    with pytest.raises(ValueError):
+        _desc(rp, num_heads=2**31)        # never narrowed
+    with pytest.raises(ValueError):
+        rp.dtype_code("int4")
+
+
+def test_debug_encode_rows_validation(rp):
+    d = _desc(rp, state_dtype="i8", dstate=16, dim=16)
+    st = rp.lib().rssm_debug_encode_rows(ctypes.byref(d), 0x10000, 0x10000, None, 0x10000, 0x10000, 4, None)
+    assert st == 2
+    d = _desc(rp, state_dtype="bf16")
+    assert rp.lib().rssm_debug_encode_rows(ctypes.byref(d), None, None, None, None, None, -1, None) == 1
+    assert rp.lib().rssm_debug_encode_rows(ctypes.byref(d), None, None, None, None, None, 0, None) == 0
+
+
+def test_caller_examples_from_the_pages(rp):
+    rows = [l.split() for l in open(os.path.join(ROOT, "tests", "golden", "caller_examples.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) == 2
+    for pos, buffered, period, expected in rows:
+        assert rp.checkpoint_prefix_len(int(pos), int(buffered), int(period)) == int(expected)
+    assert rp.checkpoint_prefix_len(120, 3, 128) is None
+
+
+def test_algorithmic_bytes_formula():
+    """Per written (layer, request): 2*H*dim*dstate*s_b state bytes plus
+    k*(H*dim + G*dstate)*i_b + k*H*4 ring bytes (for the large bf16
+    workload: 8,388,608 + k*35,840), plus H*4 bytes of A per layer."""
+    import rssm_inputs as ri
+    import rssm_harness as hx
+    spec = ri.CONFIGS["large_bf16"]
+    meta = ri.make_meta(spec, np.random.default_rng(0), n_active=3)
+    k = meta.prefix[meta.active[:3]]
+    want = sum(spec.L * (8_388_608 + int(kk) * 35_840) for kk in k) + spec.L * spec.H * 4
+    assert hx.algorithmic_bytes(spec, meta) == want

@@ -1,0 +1,347 @@
+"""GPU parity: librssm_materialize (through its C ABI) against the CPU oracle.
+
+Every case draws seeded inputs from rssm_inputs, runs the oracle on the host
+and the HIP path on the device, and compares element by element with the
+tolerances of tests/parity.py.  Full-size workloads are checked on sampled
+tiles that the oracle computes one by one, in the launch configuration the
+benchmark times.
+"""
+import hashlib
+import sys
+
+import numpy as np
+import pytest
+
+import rssm_inputs as ri
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import replayssm_persistent_rssm_amd as rp  # noqa: F401  (fails loudly if the library is missing)
+    return torch.device("cuda:0")
+
+
+def run_gpu(prob, dev, max_workgroups=0, active=None):
+    import torch
+    import rssm_harness as hx
+    dp = hx.upload(prob, dev)
+    tabs = hx.tables(dp, dev)
+    act = None
+    if active is not None:
+        act = torch.from_numpy(np.ascontiguousarray(active, np.int32)).to(dev)
+    hx.materialize(dp, tabs, max_workgroups=max_workgroups, active=act)
+    torch.cuda.synchronize()
+    st = hx.download(dp.state, prob.state)
+    sc = hx.download(dp.scale, prob.scale) if prob.scale else None
+    ring = [hx.download(dp.x, prob.x), hx.download(dp.Bm, prob.Bm), hx.download(dp.dt, prob.dt),
+            hx.download(dp.A, prob.A)]
+    return st, sc, ring
+
+
+def check(prob, dev, **kw):
+    import parity
+    st, sc, ring = run_gpu(prob, dev, **kw)
+    for got, want in zip(ring, [prob.x, prob.Bm, prob.dt, prob.A]):
+        for g, w in zip(got, want):
+            assert np.array_equal(g.view(np.uint8), w.view(np.uint8)), "ring or A changed"
+    parity.check_against_oracle(prob, st, sc)
+    return st, sc
+
+
+# --------------------------------------------------------------------------
+# The workloads' own shapes (small ones whole; large ones scaled down here,
+# sampled at full size below)
+# --------------------------------------------------------------------------
+def test_tiny_f32_workload(dev):
+    spec = ri.CONFIGS["tiny_f32"]
+    say("tiny_f32 seed 1000", spec)
+    check(ri.make_problem(spec, 1000), dev)
+
+
+def test_mid_bf16_workload(dev):
+    spec = ri.CONFIGS["mid_bf16"]
+    say("mid_bf16 seed 1001 (distinct strides per layer)")
+    check(ri.make_problem(spec, 1001), dev)
+
+
+SCALED = {
+    "large_bf16": dict(L=3, B=8, H=64, n_active=5, slots=16, ring_slots=8),
+    "large_i8": dict(L=2, B=8, H=64, n_active=6, slots=16, ring_slots=8),
+    "large_f8sr": dict(L=2, B=8, H=32, n_active=5, slots=16, ring_slots=8),
+}
+
+
+@pytest.mark.parametrize("name", list(SCALED))
+def test_large_workloads_scaled(dev, name):
+    spec = ri.scaled(ri.CONFIGS[name], name + "_scaled", **SCALED[name])
+    say(name, "scaled", SCALED[name])
+    check(ri.make_problem(spec, 1002 + list(SCALED).index(name)), dev)
+
+
+# --------------------------------------------------------------------------
+# dtype matrix on the 64x128 tile, plus the 16x16 tile
+# --------------------------------------------------------------------------
+MATRIX = ri.Spec("matrix", L=2, B=3, H=8, hpg=4, dim=64, dstate=128, R=8, W=8, k_lo=0, k_hi=8,
+                 slots=6, ring_slots=6, slot_mode="perm", stride_pad="per_layer", rand_seed=77)
+
+
+@pytest.mark.parametrize("state", ["f32", "bf16", "f16", "i8", "f8e4m3"])
+@pytest.mark.parametrize("inp", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("rounds", [0, 10])
+def test_dtype_matrix(dev, state, inp, rounds):
+    if state == "f32" and rounds:
+        pytest.skip("fp32 state is never rounded")
+    spec = ri.with_(MATRIX, state_dtype=state, input_dtype=inp, philox_rounds=rounds)
+    say("matrix", state, inp, rounds)
+    check(ri.make_problem(spec, 2000 + ri.DTYPE_CODE[state] * 10 + ri.DTYPE_CODE[inp]), dev)
+
+
+@pytest.mark.parametrize("state", ["f32", "bf16", "f16"])
+def test_small_tile_16x16(dev, state):
+    spec = ri.with_(ri.CONFIGS["tiny_f32"], name="t16", L=2, B=5, H=6, hpg=3, state_dtype=state,
+                    input_dtype="bf16", ring_start=None, prefix=None, k_lo=0, k_hi=8, slots=10, ring_slots=10,
+                    slot_mode="perm", src_fixed=None, dst_fixed=None, stride_pad="per_layer",
+                    active_order="random", philox_rounds=7 if state != "f32" else 0, rand_seed=5)
+    say("16x16", state)
+    check(ri.make_problem(spec, 2100 + ri.DTYPE_CODE[state]), dev)
+
+
+def test_window_16_and_short_ring(dev):
+    """max_window 16 (the wide-register instance) with a ring shorter than the
+    window: entries wrap more than once."""
+    spec = ri.with_(MATRIX, W=16, R=5, k_lo=9, k_hi=16, state_dtype="bf16", input_dtype="bf16")
+    say("W=16 R=5")
+    check(ri.make_problem(spec, 2200), dev)
+
+
+# --------------------------------------------------------------------------
+# Edge cases
+# --------------------------------------------------------------------------
+def test_no_active_request(dev):
+    prob = ri.make_problem(ri.with_(MATRIX, n_active=0), 2300)
+    say("n_active=0")
+    check(prob, dev)
+
+
+def test_all_pad_and_nondefault_pad(dev):
+    spec = ri.with_(MATRIX, pad_slot_id=3, slot_mode="fixed", src_fixed=[0, 3, 1], dst_fixed=[4, 5, 3],
+                    stride_pad="none")
+    prob = ri.make_problem(spec, 2301)
+    say("pad_slot_id=3, slot 0 valid")
+    check(prob, dev)
+    prob2 = ri.make_problem(ri.with_(MATRIX, pad_frac=1.0), 2302)
+    say("every pair padded")
+    check(prob2, dev)
+
+
+def test_entries_after_first_terminator_ignored(dev):
+    prob = ri.make_problem(ri.with_(MATRIX, n_active=3), 2303)
+    prob.meta.active[1] = -1                  # only the first request counts
+    say("garbage after -1")
+    check(prob, dev)
+
+
+def test_ragged_batch_across_wave_boundaries(dev):
+    """B = 70 (spans two 64-entry ballots) with 69 active, tiny tiles: the
+    work does not divide the grid."""
+    spec = ri.with_(ri.CONFIGS["tiny_f32"], name="ragged", L=2, B=70, H=2, hpg=1, ring_start=None,
+                    prefix=None, k_lo=0, k_hi=8, slots=140, ring_slots=140, slot_mode="perm",
+                    src_fixed=None, dst_fixed=None, n_active=69, active_order="random")
+    say("ragged B=70 n=69")
+    check(ri.make_problem(spec, 2304), dev)
+
+
+def _digest(arrs):
+    h = hashlib.sha256()
+    for a in arrs:
+        h.update(np.ascontiguousarray(a).view(np.uint8).tobytes())
+    return h.hexdigest()
+
+
+@pytest.mark.parametrize("state,rounds", [("bf16", 0), ("f8e4m3", 10), ("i8", 10)])
+def test_grid_and_order_invariance(dev, state, rounds):
+    """Results do not depend on the persistent grid size or on the order of
+    the active prefix (Philox keys use the physical request index)."""
+    spec = ri.with_(MATRIX, state_dtype=state, input_dtype="bf16", philox_rounds=rounds, B=5, slots=10,
+                    ring_slots=10, n_active=4)
+    prob = ri.make_problem(spec, 2400)
+    digests = set()
+    for mw in (0, 1, 2, 7, 1000):
+        say("grid", mw, state)
+        st, sc, _ = run_gpu(prob, dev, max_workgroups=mw)
+        digests.add(_digest(st + (sc or [])))
+    act = prob.meta.active.copy()
+    act[:4] = act[:4][::-1]
+    st, sc, _ = run_gpu(prob, dev, active=act)
+    digests.add(_digest(st + (sc or [])))
+    assert len(digests) == 1
+
+
+# --------------------------------------------------------------------------
+# Rounding: bit-exact against the oracle when pre-rounding values agree
+# --------------------------------------------------------------------------
+def _exact_arithmetic(prob):
+    """A = 0, dt = 2^-4, x small integers, B integers / 16, state a multiple
+    of 2^-8 (one-byte: power-of-two row scales): every fp32 value on both
+    sides is exact, so codes must agree bit for bit."""
+    rng = np.random.default_rng(99)
+    s = prob.spec
+    for l in range(s.L):
+        prob.A[l][:] = 0.0
+        prob.dt[l][:] = 2.0 ** -4
+        xv = rng.integers(-3, 4, size=prob.x[l].shape).astype(np.float32)
+        bv = (rng.integers(-8, 9, size=prob.Bm[l].shape) / 16.0).astype(np.float32)
+        prob.x[l][:] = ri._to_storage(xv, s.input_dtype)
+        prob.Bm[l][:] = ri._to_storage(bv, s.input_dtype)
+        if ri.one_byte(s.state_dtype):
+            prob.scale[l][:] = 2.0 ** -5
+        else:
+            sv = (rng.integers(-1024, 1025, size=prob.state[l].shape) / 256.0).astype(np.float32)
+            prob.state[l][:] = ri._to_storage(sv, s.state_dtype)
+    return prob
+
+
+@pytest.mark.parametrize("state", ["bf16", "f16", "i8", "f8e4m3"])
+@pytest.mark.parametrize("rounds", [0, 10])
+def test_rounding_bit_exact_on_exact_inputs(dev, state, rounds):
+    import oracle
+    spec = ri.with_(MATRIX, state_dtype=state, input_dtype="bf16", philox_rounds=rounds, rand_seed=1234)
+    prob = _exact_arithmetic(ri.make_problem(spec, 2500))
+    say("bit-exact rounding", state, rounds)
+    st, sc, _ = run_gpu(prob, dev)
+    st_o, sc_o, _, _ = oracle.materialize(prob)
+    for l in range(spec.L):
+        assert np.array_equal(st[l].view(np.uint8), st_o[l].view(np.uint8)), f"layer {l} codes differ"
+        if sc is not None:
+            assert np.array_equal(sc[l].view(np.uint32), sc_o[l].view(np.uint32)), f"layer {l} scales differ"
+
+
+@pytest.mark.parametrize("state", ["bf16", "f16", "i8", "f8e4m3"])
+@pytest.mark.parametrize("rounds", [0, 10])
+@pytest.mark.parametrize("dstate", [16, 128])
+def test_debug_encode_rows_bit_exact(dev, state, rounds, dstate):
+    """The kernel's encode step on arbitrary fp32 rows equals the oracle's,
+    code for code (nearest-even and Philox stochastic rounding)."""
+    import torch
+    import oracle
+    from replayssm_persistent_rssm_amd import rssm_debug_encode_rows
+    if ri.one_byte(state) and dstate != 128:
+        pytest.skip("one-byte state rows have 128 columns")
+    rng = np.random.default_rng(3000 + dstate + rounds)
+    n = 96
+    rows = (rng.standard_normal((n, dstate)) * np.exp(rng.uniform(-12, 12, (n, 1)))).astype(np.float32)
+    rows[0] = 0.0
+    rows[1, :] = np.float32(1.0 + 2.0 ** -8)           # bf16 tie
+    rows[2, :] = np.float32(2.0 ** -130)               # fp32 subnormal
+    rows[3, :dstate // 2] = np.float32(70000.0)        # fp16 overflow / saturation
+    rows[4] = rng.standard_normal(dstate).astype(np.float32) * 1e-8
+    coords = np.stack([rng.integers(0, 48, n), rng.integers(0, 256, n), rng.integers(0, 256, n),
+                       rng.integers(0, 64, n)], 1).astype(np.int32)
+    seed = 0x123456789ABCDEF
+    spec = ri.with_(MATRIX, dstate=dstate, state_dtype=state, philox_rounds=rounds, rand_seed=seed)
+    say("encode rows", state, rounds, dstate)
+    t_rows = torch.from_numpy(rows).to(dev)
+    t_coords = torch.from_numpy(coords).to(dev)
+    t_seed = torch.tensor([seed], dtype=torch.int64, device=dev)
+    eb = ri.ELEM_BYTES[state]
+    out = torch.zeros((n, dstate * eb), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((n,), dtype=torch.float32, device=dev) if ri.one_byte(state) else None
+    rssm_debug_encode_rows(t_rows, t_coords, t_seed if rounds else None, out, scales, state_dtype=state,
+                           dstate=dstate, philox_rounds=rounds)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i in range(n):
+        l, b, h, r = (int(v) for v in coords[i])
+        codes, scale = oracle.encode_row(spec, rows[i], l, b, h, r)
+        assert np.array_equal(got[i], codes.view(np.uint8)), f"row {i} ({l},{b},{h},{r})"
+        if scales is not None:
+            assert np.float32(scales[i].item()).view(np.uint32) == np.float32(scale).view(np.uint32), f"row {i} scale"
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads, sampled (launch configuration of the benchmark)
+# --------------------------------------------------------------------------
+def _sampled_full_size(dev, name, n_active, seed, n_samples=24):
+    import torch
+    import oracle
+    import parity
+    import rssm_harness as hx
+    spec = ri.CONFIGS[name]
+    say("full size", name, "n_active", n_active, "seed", seed)
+    dp = ri.make_device_problem(spec, seed, dev, n_active=n_active)
+    tabs = hx.tables(dp, dev)
+    torch.cuda.synchronize()
+    m = dp.meta
+    srcs = sorted(set(int(v) for v in m.src.reshape(-1) if v != spec.pad_slot_id))
+    before = [int(t[srcs].view(torch.int32).to(torch.int64).sum().item()) for t in dp.state]
+    hx.materialize(dp, tabs)
+    torch.cuda.synchronize()
+    after = [int(t[srcs].view(torch.int32).to(torch.int64).sum().item()) for t in dp.state]
+    assert before == after, "source slots changed"
+
+    rng = np.random.default_rng(seed)
+    n_tile = spec.dim * spec.dstate
+    _, _, d_x, d_B, d_dt = ri.dense_sizes(spec)
+    picks = [(0, 0, 0), (n_active - 1, spec.L - 1, spec.H - 1)]
+    picks += [(int(rng.integers(n_active)), int(rng.integers(spec.L)), int(rng.integers(spec.H)))
+              for _ in range(n_samples)]
+    np_dt = ri.STORAGE_NP[spec.state_dtype]
+    for i, l, h in picks:
+        b = int(m.active[i])
+        s, d = int(m.src[l, b]), int(m.dst[l, b])
+        k, r0 = int(m.prefix[b]), int(m.ring_start[b])
+        def host(t, sl):
+            a = t[sl].cpu()
+            if a.dtype == torch.bfloat16:
+                a = a.view(torch.int16)
+            return a.numpy()
+        src_tile = host(dp.state[l], (s, slice(h * n_tile, (h + 1) * n_tile))).view(np_dt)
+        gpu_tile = host(dp.state[l], (d, slice(h * n_tile, (h + 1) * n_tile))).view(np_dt)
+        src_sc = gpu_sc = None
+        if dp.scale:
+            src_sc = host(dp.scale[l], (s, slice(h * spec.dim, (h + 1) * spec.dim)))
+            gpu_sc = host(dp.scale[l], (d, slice(h * spec.dim, (h + 1) * spec.dim)))
+        x_slot = host(dp.x[l], (s, slice(0, d_x))).view(ri.STORAGE_NP[spec.input_dtype])
+        B_slot = host(dp.Bm[l], (s, slice(0, d_B))).view(ri.STORAGE_NP[spec.input_dtype])
+        dt_slot = host(dp.dt[l], (s, slice(0, d_dt)))
+        A_h = float(dp.A[l][h].item())
+        codes, scale, exact, mag = oracle.tile(spec, l, b, h, r0, k, A_h, src_tile, src_sc, x_slot, B_slot, dt_slot)
+        what = f"{name} i={i} b={b} l={l} h={h} k={k}"
+        if k == 0:
+            assert np.array_equal(gpu_tile.view(np.uint8), src_tile.view(np.uint8)), what
+            if gpu_sc is not None:
+                assert np.array_equal(gpu_sc.view(np.uint32), src_sc.view(np.uint32)), what
+        else:
+            parity.compare_tile(spec.state_dtype, gpu_tile, codes, exact, mag, gpu_sc, scale, what)
+    # destination slots of requests that are not listed keep their fill bytes
+    listed = set(int(v) for v in m.active[:n_active])
+    free_dst = sorted(set(range(spec.B, 2 * spec.B)) - set(int(v) for v in m.dst.reshape(-1)))
+    if free_dst:
+        for l in (0, spec.L - 1):
+            t = dp.state[l][free_dst[:4]].view(torch.uint8)
+            assert bool((t == 0xA5).all().item()), "an unlisted destination slot was written"
+    del dp, tabs
+    torch.cuda.empty_cache()
+    return listed
+
+
+@pytest.mark.parametrize("n_active", [256, 16])
+def test_full_size_large_bf16_sampled(dev, n_active):
+    _sampled_full_size(dev, "large_bf16", n_active, 1000 + 2 * 10 + n_active % 7)
+
+
+def test_full_size_large_i8_sampled(dev):
+    _sampled_full_size(dev, "large_i8", 64, 1003)
+
+
+def test_full_size_large_f8sr_sampled(dev):
+    _sampled_full_size(dev, "large_f8sr", 128, 1004)
