@@ -151,19 +151,13 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def rssm_materialize(state_ptrs, state_slot_strides, x_cache_ptrs, x_cache_slot_strides, B_cache_ptrs,
-                     B_cache_slot_strides, dt_cache_ptrs, dt_cache_slot_strides, A_ptrs, state_scale_ptrs,
-                     state_scale_slot_strides, src_slots, dst_slots, ring_start, replay_prefix_len,
-                     active_request_indices, *, state_dtype, input_dtype, matrixA_dtype, dim: int, dstate: int,
-                     num_heads: int, heads_per_group: int, max_window: int, ring_buffer_len: int,
-                     pad_slot_id: int = -1, rand_seed=None, philox_rounds: int = 0, max_workgroups: int = 0,
-                     stream=None) -> None:
-    """Enqueue one materialize call (keyword names of the page's signature).
-
-    Per-layer tables are device int64 tensors of shape (L,); src_slots and
-    dst_slots device int32 (L, B); ring_start, replay_prefix_len and
-    active_request_indices device int32 (B,); rand_seed a device int64 (1,)
-    tensor.  Enqueued on `stream` (default: torch's current stream)."""
+def _marshal(state_ptrs, state_slot_strides, x_cache_ptrs, x_cache_slot_strides, B_cache_ptrs,
+             B_cache_slot_strides, dt_cache_ptrs, dt_cache_slot_strides, A_ptrs, state_scale_ptrs,
+             state_scale_slot_strides, src_slots, dst_slots, ring_start, replay_prefix_len,
+             active_request_indices, *, state_dtype, input_dtype, matrixA_dtype, dim: int, dstate: int,
+             num_heads: int, heads_per_group: int, max_window: int, ring_buffer_len: int, pad_slot_id: int = -1,
+             rand_seed=None, philox_rounds: int = 0, max_workgroups: int = 0):
+    """Check host-visible tensor metadata and build the C descriptor and tables."""
     import torch
     L = int(state_ptrs.shape[0])
     Bsz = int(ring_start.shape[0])
@@ -183,7 +177,8 @@ def rssm_materialize(state_ptrs, state_slot_strides, x_cache_ptrs, x_cache_slot_
         dt_ptrs=_ptr(dt_cache_ptrs, "dt_cache_ptrs", i64, (L,)),
         dt_slot_strides=_ptr(dt_cache_slot_strides, "dt_cache_slot_strides", i64, (L,)),
         A_ptrs=_ptr(A_ptrs, "A_ptrs", i64, (L,)),
-        scale_ptrs=_ptr(state_scale_ptrs, "state_scale_ptrs", i64, (L,)) if quant or state_scale_ptrs is not None else None,
+        scale_ptrs=_ptr(state_scale_ptrs, "state_scale_ptrs", i64, (L,))
+        if quant or state_scale_ptrs is not None else None,
         scale_slot_strides=_ptr(state_scale_slot_strides, "state_scale_slot_strides", i64, (L,))
         if quant or state_scale_slot_strides is not None else None,
         src_slots=_ptr(src_slots, "src_slots", i32, (L, Bsz)),
@@ -192,11 +187,58 @@ def rssm_materialize(state_ptrs, state_slot_strides, x_cache_ptrs, x_cache_slot_
         replay_prefix_len=_ptr(replay_prefix_len, "replay_prefix_len", i32, (Bsz,)),
         active_request_indices=_ptr(active_request_indices, "active_request_indices", i32, (Bsz,)),
         rand_seed=_ptr(rand_seed, "rand_seed", i64, (1,)) if rand_seed is not None else None)
+    return desc, tab
+
+
+def rssm_materialize(*args, stream=None, **kw) -> None:
+    """Enqueue one materialize call.
+
+    Positional arguments, in the page's order: state_ptrs, state_slot_strides,
+    x_cache_ptrs, x_cache_slot_strides, B_cache_ptrs, B_cache_slot_strides,
+    dt_cache_ptrs, dt_cache_slot_strides, A_ptrs, state_scale_ptrs,
+    state_scale_slot_strides, src_slots, dst_slots, ring_start,
+    replay_prefix_len, active_request_indices.  Keywords: state_dtype,
+    input_dtype, matrixA_dtype, dim, dstate, num_heads, heads_per_group,
+    max_window, ring_buffer_len, pad_slot_id=-1, rand_seed=None,
+    philox_rounds=0, max_workgroups=0.
+
+    Per-layer tables are device int64 tensors of shape (L,); src_slots and
+    dst_slots device int32 (L, B); ring_start, replay_prefix_len and
+    active_request_indices device int32 (B,); rand_seed a device int64 (1,)
+    tensor.  Enqueued on `stream` (default: torch's current stream)."""
+    desc, tab = _marshal(*args, **kw)
     _check(_lib.rssm_materialize(ctypes.byref(desc), ctypes.byref(tab), _stream_handle(stream)))
 
 
 # The page's name for the same call.
 replayssm_materialize = rssm_materialize
+
+
+class MaterializeCall:
+    """A prepared rssm_materialize: the arguments are checked and marshalled
+    once, and each call is one C call with the stored descriptor and tables.
+
+    Same arguments as rssm_materialize; stream=None binds torch's current
+    stream at construction.  The caller keeps every tensor alive while the
+    object is used.  A call may pass another device int32 tensor of shape
+    (B,) as the active list."""
+
+    def __init__(self, *args, stream=None, **kw):
+        self._desc, self._tab = _marshal(*args, **kw)
+        self._desc_ref = ctypes.byref(self._desc)
+        self._tab_ref = ctypes.byref(self._tab)
+        self._stream = _stream_handle(stream)
+        self._batch = int(self._desc.batch)
+        self._fn = _lib.rssm_materialize
+
+    def __call__(self, active_request_indices=None) -> None:
+        if active_request_indices is not None:
+            import torch
+            self._tab.active_request_indices = _ptr(active_request_indices, "active_request_indices",
+                                                    torch.int32, (self._batch,))
+        st = self._fn(self._desc_ref, self._tab_ref, self._stream)
+        if st != RSSM_OK:
+            raise RssmError(st, rssm_last_error())
 
 
 def rssm_materialize_launch_config(**desc_kw):

@@ -231,6 +231,16 @@ rssm_status grid_for(const void* fn, int* grid_out) {
   return RSSM_OK;
 }
 
+// The last descriptor validated on this thread, with its instance and grid
+// on that device: a serving loop calls with the same scalars every step.
+struct LaunchCache {
+  rssm_materialize_desc desc;
+  int device = -1;
+  const rssm::KernelEntry* kernel = nullptr;
+  int grid = 0;
+};
+thread_local LaunchCache g_last;
+
 int lds_bytes_of(const rssm_materialize_desc* d) {
   const int kmax = d->max_window <= 8 ? 8 : 16;
   return rssm::kWaves * d->dim * kmax * static_cast<int>(sizeof(float));
@@ -267,18 +277,40 @@ rssm_status rssm_materialize_launch_config(const rssm_materialize_desc* desc, in
 rssm_status rssm_materialize(const rssm_materialize_desc* desc, const rssm_materialize_tables* tables,
                              void* hip_stream) {
   g_err[0] = '\0';
-  rssm_status st = validate_desc(desc);
-  if (st != RSSM_OK) return st;
+  if (desc == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const rssm::KernelEntry* k = nullptr;
+  int grid = 0;
+  rssm_status st;
+  const bool same_desc = g_last.kernel != nullptr &&
+                         std::memcmp(&g_last.desc, desc, sizeof(rssm_materialize_desc)) == 0;
+  // Host validation happens before any HIP call; an unchanged descriptor was
+  // validated by an earlier call on this thread.
+  if (!same_desc) {
+    st = validate_desc(desc);
+    if (st != RSSM_OK) return st;
+  }
   st = validate_tables(desc, tables);
   if (st != RSSM_OK) return st;
-  const rssm::KernelEntry* k = find_kernel(desc);
-  if (k == nullptr)
-    return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance for state=%s input=%s dim=%d dstate=%d",
-                dtype_name(desc->state_dtype), dtype_name(desc->input_dtype), desc->dim, desc->dstate);
-  int grid = desc->max_workgroups;
-  if (grid == 0) {
-    st = grid_for(k->fn, &grid);
-    if (st != RSSM_OK) return st;
+  int dev = 0;
+  hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return fail(RSSM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(de));
+  if (same_desc && g_last.device == dev) {
+    k = g_last.kernel;
+    grid = g_last.grid;
+  } else {
+    k = find_kernel(desc);
+    if (k == nullptr)
+      return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance for state=%s input=%s dim=%d dstate=%d",
+                  dtype_name(desc->state_dtype), dtype_name(desc->input_dtype), desc->dim, desc->dstate);
+    grid = desc->max_workgroups;
+    if (grid == 0) {
+      st = grid_for(k->fn, &grid);
+      if (st != RSSM_OK) return st;
+    }
+    g_last.desc = *desc;
+    g_last.device = dev;
+    g_last.kernel = k;
+    g_last.grid = grid;
   }
   rssm::KernelArgs args;
   args.state_ptrs = tables->state_ptrs;

@@ -103,6 +103,23 @@ def materialize(dp: ri.DeviceProblem, tabs: Tables, max_workgroups: int = 0, str
         rand_seed=tabs.rand_seed, philox_rounds=s.philox_rounds, max_workgroups=max_workgroups, stream=stream)
 
 
+def prepared(dp: ri.DeviceProblem, tabs: Tables, max_workgroups: int = 0, stream=None,
+             replay_prefix_len=None):
+    """A MaterializeCall for a device problem: marshalled once, one C call per
+    invocation (optionally with another prefix-length tensor)."""
+    from replayssm_persistent_rssm_amd import MaterializeCall
+    s = dp.spec
+    return MaterializeCall(
+        tabs.state_ptrs, tabs.state_slot_strides, tabs.x_cache_ptrs, tabs.x_cache_slot_strides,
+        tabs.B_cache_ptrs, tabs.B_cache_slot_strides, tabs.dt_cache_ptrs, tabs.dt_cache_slot_strides,
+        tabs.A_ptrs, tabs.state_scale_ptrs, tabs.state_scale_slot_strides, tabs.src_slots, tabs.dst_slots,
+        tabs.ring_start, tabs.replay_prefix_len if replay_prefix_len is None else replay_prefix_len,
+        tabs.active_request_indices,
+        state_dtype=s.state_dtype, input_dtype=s.input_dtype, matrixA_dtype="f32", dim=s.dim, dstate=s.dstate,
+        num_heads=s.H, heads_per_group=s.hpg, max_window=s.W, ring_buffer_len=s.R, pad_slot_id=s.pad_slot_id,
+        rand_seed=tabs.rand_seed, philox_rounds=s.philox_rounds, max_workgroups=max_workgroups, stream=stream)
+
+
 def algorithmic_bytes(spec: ri.Spec, meta: ri.Meta, n_active: Optional[int] = None) -> int:
     """Bytes the method itself must move for one call: per written (layer,
     request) the state in and out (+ row scales for one-byte state) and, for
