@@ -173,6 +173,8 @@ def main():
     torch.cuda.synchronize()
     ms = timed_calls(call, args.steps, stream)
     torch.cuda.synchronize()
+    # spread of single calls (outside the timed region)
+    singles = sorted(timed_calls(call, 1, stream) for _ in range(5))
     value = full_bytes / (ms * 1e-3) / 1e9
     say(f"full batch: {ms:.3f} ms/call, {value:.1f} GB/s")
     result = {
@@ -188,6 +190,7 @@ def main():
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(full_bytes),
                      "kernel": "materialize_kernel<bf16,bf16,64x128,kmax8>", "kernel_source_hash": kernel_hash()},
         "us_per_request_full": round(ms * 1e3 / spec.B, 3),
+        "single_call_ms_min_med_max": [round(singles[0], 3), round(singles[2], 3), round(singles[-1], 3)],
     }
     if args.only_main:
         print(json.dumps(result), flush=True)

@@ -34,33 +34,49 @@ template <int DT> constexpr bool kOneByte = (DT == kI8 || DT == kF8);
 // 8 consecutive elements of one row ("chunk") in raw storage: 8/4/2 dwords.
 template <int DT> struct Chunk { uint32_t w[2 * Fmt<DT>::bytes]; };
 
-template <int DT>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const char* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
+}
+
+template <bool NT, typename V>
+__device__ __forceinline__ void st(char* p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  else *reinterpret_cast<V*>(p) = v;
+}
+
+// NT: non-temporal (streaming) access, for data read or written once.
+template <int DT, bool NT = false>
 __device__ __forceinline__ Chunk<DT> load_chunk(const char* p) {
   Chunk<DT> c;
   if constexpr (Fmt<DT>::bytes == 4) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
+    const u32x4 a = ld<NT, u32x4>(p);
+    const u32x4 b = ld<NT, u32x4>(p + 16);
     c.w[0] = a.x; c.w[1] = a.y; c.w[2] = a.z; c.w[3] = a.w;
     c.w[4] = b.x; c.w[5] = b.y; c.w[6] = b.z; c.w[7] = b.w;
   } else if constexpr (Fmt<DT>::bytes == 2) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const u32x4 a = ld<NT, u32x4>(p);
     c.w[0] = a.x; c.w[1] = a.y; c.w[2] = a.z; c.w[3] = a.w;
   } else {
-    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    const u32x2 a = ld<NT, u32x2>(p);
     c.w[0] = a.x; c.w[1] = a.y;
   }
   return c;
 }
 
-template <int DT>
+template <int DT, bool NT = false>
 __device__ __forceinline__ void store_chunk(char* p, const Chunk<DT>& c) {
   if constexpr (Fmt<DT>::bytes == 4) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
-    *reinterpret_cast<uint4*>(p + 16) = make_uint4(c.w[4], c.w[5], c.w[6], c.w[7]);
+    st<NT>(p, u32x4{c.w[0], c.w[1], c.w[2], c.w[3]});
+    st<NT>(p + 16, u32x4{c.w[4], c.w[5], c.w[6], c.w[7]});
   } else if constexpr (Fmt<DT>::bytes == 2) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+    st<NT>(p, u32x4{c.w[0], c.w[1], c.w[2], c.w[3]});
   } else {
-    *reinterpret_cast<uint2*>(p) = make_uint2(c.w[0], c.w[1]);
+    st<NT>(p, u32x2{c.w[0], c.w[1]});
   }
 }
 
