@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 WORKLOAD = "large_bf16"
 SEED = 1002
+SEEDS = {"large_bf16": 1002, "large_i8": 1003, "large_f8sr": 1004}
 KERNEL_SOURCES = ["replayssm_persistent_rssm_amd/csrc/rssm_kernel.h",
                   "replayssm_persistent_rssm_amd/csrc/rssm_device.h"]
 
@@ -124,6 +125,10 @@ def main():
     ap.add_argument("--empty-only", action="store_true", help="profile mode: 200 calls with no active request")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="counter mode: 2 full-batch calls, then 2 plain device copies of 1 GiB")
+    ap.add_argument("--workload", default=WORKLOAD, choices=["large_bf16", "large_i8", "large_f8sr"],
+                    help="workload of the profile modes (the headline line always uses large_bf16)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the int8 and e4m3+Philox workload lines")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path needs no collectives and every run here uses a "
@@ -136,10 +141,12 @@ def main():
     import replayssm_persistent_rssm_amd as rp
 
     dev = torch.device("cuda:0")
-    spec = ri.CONFIGS[WORKLOAD]
-    say("generating", WORKLOAD, "seed", SEED)
+    profile_mode = args.only_main or args.empty_only or args.pmc_calibrate
+    wl = args.workload if profile_mode else WORKLOAD
+    spec = ri.CONFIGS[wl]
+    say("generating", wl, "seed", SEEDS[wl])
     t0 = time.time()
-    dp = ri.make_device_problem(spec, SEED, dev, n_active=spec.B, fill_dst=0)
+    dp = ri.make_device_problem(spec, SEEDS[wl], dev, fill_dst=0)
     tabs = hx.tables(dp, dev)
     torch.cuda.synchronize()
     say(f"inputs resident in HBM ({time.time() - t0:.1f} s)")
@@ -287,7 +294,43 @@ def main():
     if not args.no_cpu_baseline:
         say(f"CPU oracle sample (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(dp, args.cpu_seconds)
+
+    if not args.no_other_workloads:
+        del call, tabs, dp
+        torch.cuda.empty_cache()
+        result["other_workloads"] = {name: other_workload(name, dev, stream, max(5, args.steps // 2))
+                                     for name in ("large_i8", "large_f8sr")}
     print(json.dumps(result), flush=True)
+
+
+def other_workload(name, dev, stream, steps):
+    """Time one call of a secondary workload (its listed requests active)."""
+    import torch
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    spec = ri.CONFIGS[name]
+    say("generating", name, "seed", SEEDS[name])
+    dp = ri.make_device_problem(spec, SEEDS[name], dev, fill_dst=0)
+    tabs = hx.tables(dp, dev)
+    call = hx.prepared(dp, tabs)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ms = timed_calls(call, steps, stream)
+    nbytes = hx.algorithmic_bytes(spec, dp.meta)
+    n = spec.n_active
+    out = {"workload": f"L={spec.L}, B={spec.B} ({n} active), H={spec.H} (hpg {spec.hpg}), "
+                       f"{spec.dim}x{spec.dstate} {spec.state_dtype} state + fp32 row scales, "
+                       f"{spec.input_dtype} x/B, R={spec.R}, max_window={spec.W}"
+                       + (f", Philox-{spec.philox_rounds} stochastic rounding" if spec.philox_rounds else ""),
+           "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+           "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "us_per_request": round(ms * 1e3 / n, 3)}
+    say(f"{name}: {out}")
+    del call, tabs, dp
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
