@@ -87,17 +87,6 @@ __device__ __forceinline__ float f16_bits_to_float(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
-// OCP e4m3fn: sign, 4 exponent bits (bias 7), 3 mantissa bits; S.1111.111 is NaN.
-__device__ __forceinline__ float e4m3_to_float(uint32_t code) {
-  const uint32_t sign = (code & 0x80u) << 24;
-  const uint32_t e = (code >> 3) & 0xFu;
-  const uint32_t m = code & 7u;
-  if (e == 0xFu && m == 7u) return __uint_as_float(sign | 0x7FC00000u);
-  const float mag = (e == 0u) ? static_cast<float>(m) * 0x1p-9f
-                              : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return __uint_as_float(__float_as_uint(mag) | sign);
-}
-
 template <int DT>
 __device__ __forceinline__ void decode_chunk(const Chunk<DT>& c, float (&f)[8]) {
   if constexpr (DT == kF32) {
@@ -120,8 +109,17 @@ __device__ __forceinline__ void decode_chunk(const Chunk<DT>& c, float (&f)[8]) 
     for (int i = 0; i < 8; ++i)
       f[i] = static_cast<float>(static_cast<int8_t>((c.w[i >> 2] >> (8 * (i & 3))) & 0xFFu));
   } else {
+    // OCP e4m3fn (sign, 4 exponent bits with bias 7, 3 mantissa bits; only
+    // S.1111.111 is NaN): gfx950's fp8 conversion instructions use this format.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = e4m3_to_float((c.w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    for (int i = 0; i < 2; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c.w[i]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c.w[i]), true);
+      f[4 * i + 0] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
   }
 }
 
@@ -131,18 +129,43 @@ __device__ __forceinline__ void decode_chunk(const Chunk<DT>& c, float (&f)[8]) 
 // two odd multipliers; new counter (hi1^c1^k0, lo1, hi0^c3^k1, lo0); the key
 // advances by the Weyl increments between rounds.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint4 philox4x32(uint4 c, uint32_t k0, uint32_t k1, int rounds) {
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                             uint32_t k0, uint32_t k1) {
   constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  const uint64_t p0 = static_cast<uint64_t>(kM0) * c0;
+  const uint64_t p1 = static_cast<uint64_t>(kM1) * c2;
+  const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+  const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+  c1 = static_cast<uint32_t>(p1);
+  c3 = static_cast<uint32_t>(p0);
+  c0 = n0;
+  c2 = n2;
+}
+
+// Two Philox4x32-R blocks with counters (x, y, z, w) and (x + 1, y, z, w),
+// interleaved for instruction-level parallelism; rounds are unrolled by two.
+__device__ __forceinline__ void philox4x32_pair(uint32_t x, uint32_t y, uint32_t z, uint32_t w, uint32_t k0,
+                                                uint32_t k1, int rounds, uint32_t (&u)[8]) {
   constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
-  for (int i = 0; i < rounds; ++i) {
-    const uint64_t p0 = static_cast<uint64_t>(kM0) * c.x;
-    const uint64_t p1 = static_cast<uint64_t>(kM1) * c.z;
-    c = make_uint4(static_cast<uint32_t>(p1 >> 32) ^ c.y ^ k0, static_cast<uint32_t>(p1),
-                   static_cast<uint32_t>(p0 >> 32) ^ c.w ^ k1, static_cast<uint32_t>(p0));
+  uint32_t a0 = x, a1 = y, a2 = z, a3 = w;
+  uint32_t b0 = x + 1u, b1 = y, b2 = z, b3 = w;
+  int i = 0;
+  for (; i + 2 <= rounds; i += 2) {
+    philox_round(a0, a1, a2, a3, k0, k1);
+    philox_round(b0, b1, b2, b3, k0, k1);
+    k0 += kW0;
+    k1 += kW1;
+    philox_round(a0, a1, a2, a3, k0, k1);
+    philox_round(b0, b1, b2, b3, k0, k1);
     k0 += kW0;
     k1 += kW1;
   }
-  return c;
+  if (i < rounds) {
+    philox_round(a0, a1, a2, a3, k0, k1);
+    philox_round(b0, b1, b2, b3, k0, k1);
+  }
+  u[0] = a0; u[1] = a1; u[2] = a2; u[3] = a3;
+  u[4] = b0; u[5] = b1; u[6] = b2; u[7] = b3;
 }
 
 // Random words of the 8 elements (r, c0..c0+7) of head h, physical request b,
@@ -150,10 +173,8 @@ __device__ __forceinline__ uint4 philox4x32(uint4 c, uint32_t k0, uint32_t k1, i
 __device__ __forceinline__ void sr_words(uint32_t (&u)[8], int r, int c0, int dstate, int h, int b,
                                          int l, uint32_t k0, uint32_t k1, int rounds) {
   const uint32_t base = static_cast<uint32_t>((static_cast<int64_t>(r) * dstate + c0) >> 2);
-  const uint4 w0 = philox4x32(make_uint4(base, h, b, l), k0, k1, rounds);
-  const uint4 w1 = philox4x32(make_uint4(base + 1u, h, b, l), k0, k1, rounds);
-  u[0] = w0.x; u[1] = w0.y; u[2] = w0.z; u[3] = w0.w;
-  u[4] = w1.x; u[5] = w1.y; u[6] = w1.z; u[7] = w1.w;
+  philox4x32_pair(base, static_cast<uint32_t>(h), static_cast<uint32_t>(b), static_cast<uint32_t>(l), k0, k1,
+                  rounds, u);
 }
 
 // ---------------------------------------------------------------------------
@@ -195,22 +216,41 @@ __device__ __forceinline__ uint32_t f16_round(float v, bool stochastic, uint32_t
   return sign | (__builtin_bit_cast(uint16_t, static_cast<_Float16>(m)) & 0x7FFFu);
 }
 
+// int8 code of t (row-scaled value): nearest-even or stochastic, saturating to
+// [-127, 127]; NaN encodes as 0 (the hardware float-to-int conversion).
 __device__ __forceinline__ uint32_t i8_round(float t, bool stochastic, uint32_t u) {
-  if (t != t) return 0u;
-  const float a = fabsf(t);
-  float q;
-  if (a >= 127.0f) {
-    q = 127.0f;
-  } else if (!stochastic) {
-    q = rintf(a);  // nearest, ties to even
+  int q;
+  if (!stochastic) {
+    q = static_cast<int>(rintf(t));
   } else {
+    const float a = fminf(fabsf(t), 127.0f);
     const float n = floorf(a);
-    q = n + (sr_up(a - n, u) ? 1.0f : 0.0f);
+    const int m = static_cast<int>(n) + (sr_up(a - n, u) ? 1 : 0);
+    q = (__float_as_uint(t) >> 31) ? -m : m;
   }
-  const int qi = (__float_as_uint(t) >> 31) ? -static_cast<int>(q) : static_cast<int>(q);
-  return static_cast<uint32_t>(qi) & 0xFFu;
+  q = min(max(q, -127), 127);
+  return static_cast<uint32_t>(q) & 0xFFu;
 }
 
+// e4m3 code of |t| < 464 (a row-scaled value; |t| <= 448(1 + 2^-22) in the
+// kernel), stochastic rounding, saturating at 448.  Normal range (|t| >= 2^-6):
+// e4m3 keeps the top 3 mantissa bits and the 20 dropped bits are f * 2^20, so
+// the rule is u < dropped << 12, and the carry of the increment moves into the
+// exponent field.  Below 2^-6 the grid spacing is 2^-9.
+__device__ __forceinline__ uint32_t e4m3_sr(float t, uint32_t u) {
+  const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
+  const float a = fabsf(t);
+  const uint32_t bits = __float_as_uint(a);
+  const uint32_t up_n = (u < ((bits & 0xFFFFFu) << 12)) ? 1u : 0u;
+  const uint32_t code_n = min((bits >> 20) - 960u + up_n, 0x7Eu);
+  const float s = a * 512.0f;
+  const float n = floorf(s);
+  const uint32_t code_s = static_cast<uint32_t>(n) + (sr_up(s - n, u) ? 1u : 0u);
+  return sign | (a >= 0x1p-6f ? code_n : code_s);
+}
+
+// General e4m3 rounding (any input): nearest-even or stochastic, saturating;
+// NaN keeps its sign with the NaN code.  Used where inputs are not row-scaled.
 __device__ __forceinline__ uint32_t e4m3_round(float t, bool stochastic, uint32_t u) {
   const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
   if (t != t) return sign | 0x7Fu;

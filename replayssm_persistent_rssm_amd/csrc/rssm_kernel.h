@@ -130,15 +130,48 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
     const float inv = qmax / m;
     const bool ok = (m > 0.0f) && !__builtin_isinf(m) && __builtin_isfinite(inv);
     row_scale = ok ? m / qmax : 0.0f;
-    uint32_t code[8];
+    float t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float t = acc[i] * inv;
-      const uint32_t c = (ST == kI8) ? i8_round(t, SR, u[i]) : e4m3_round(t, SR, u[i]);
-      code[i] = ok ? c : 0u;
+    for (int i = 0; i < 8; ++i) t[i] = acc[i] * inv;
+    if constexpr (ST == kI8) {
+      uint32_t code[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) code[i] = i8_round(t[i], SR, u[i]);
+      out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+      out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    } else {
+      // |t| <= 448(1 + 2^-22) for every finite element of a valid row.  NaN
+      // elements (ignored by the row max) take the general path.
+      bool has_nan = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) has_nan |= (t[i] != t[i]);
+      if (__builtin_expect(__ballot(has_nan) != 0, 0)) {
+        uint32_t code[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[i] = e4m3_round(t[i], SR, u[i]);
+        out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+        out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+      } else if constexpr (SR) {
+        uint32_t code[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[i] = e4m3_sr(t[i], u[i]);
+        out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+        out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+      } else {
+        // Hardware nearest-even conversion: equal to e4m3_round for |t| < 464
+        // (checked on gfx950), which covers every finite row-scaled value.
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[4 * i + 0], t[4 * i + 1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(t[4 * i + 2], t[4 * i + 3], w, true);
+          out.w[i] = static_cast<uint32_t>(w);
+        }
+      }
     }
-    out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-    out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    if (!ok) {
+      out.w[0] = 0u;
+      out.w[1] = 0u;
+    }
   }
   return out;
 }
@@ -360,8 +393,10 @@ __global__ void __launch_bounds__(kBlock, (kWavesPerSimd<KMAX, ST>)) materialize
         const float w = dtj * Pn;
         const float D = __shfl(P, 0);
 
-        // Stage w_j * x_j[r] into this wave's LDS as [row][token]; tokens
-        // k..ceil4(k)-1 are written as zero.
+        // Stage w_j * x_j[r] into this wave's LDS as [row][token].  Tokens
+        // k..ceil4(k)-1 pad the last block of four with -0.0: with B_j = +0
+        // their fused multiply-add adds -0, which leaves every accumulator
+        // unchanged (including the sign of a zero).
         const int k4 = (k + 3) & ~3;
         wave_lds_fence();
 #pragma unroll
@@ -372,16 +407,16 @@ __global__ void __launch_bounds__(kBlock, (kWavesPerSimd<KMAX, ST>)) materialize
           const int ej = __shfl(e_lane, j);
           if (idx < k4 * XCH) {
             const int r8 = (idx % XCH) * 8;
-            float xv[8];
             if (j < k) {
+              float xv[8];
               const Chunk<IT> c = load_chunk<IT>(x_slot + ((static_cast<int64_t>(ej) * a.H + h) * DIM + r8) * IB);
               decode_chunk<IT>(c, xv);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) wx[(r8 + q) * KMAX + j] = wj * xv[q];
             } else {
 #pragma unroll
-              for (int q = 0; q < 8; ++q) xv[q] = 0.0f;
+              for (int q = 0; q < 8; ++q) wx[(r8 + q) * KMAX + j] = -0.0f;
             }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) wx[(r8 + q) * KMAX + j] = wj * xv[q];
           }
         }
         wave_lds_fence();

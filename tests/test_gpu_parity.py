@@ -204,6 +204,13 @@ def _exact_arithmetic(prob):
         prob.Bm[l][:] = ri._to_storage(bv, s.input_dtype)
         if ri.one_byte(s.state_dtype):
             prob.scale[l][:] = 2.0 ** -5
+            # every finite code appears (e4m3: all but the two NaN codes)
+            n = prob.state[l].size
+            if s.state_dtype == "f8e4m3":
+                finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+            else:
+                finite = np.arange(-127, 128).astype(np.int8)
+            prob.state[l].reshape(-1)[:] = np.resize(rng.permutation(finite), n)
         else:
             sv = (rng.integers(-1024, 1025, size=prob.state[l].shape) / 256.0).astype(np.float32)
             prob.state[l][:] = ri._to_storage(sv, s.state_dtype)
@@ -218,9 +225,19 @@ def test_rounding_bit_exact_on_exact_inputs(dev, state, rounds):
     prob = _exact_arithmetic(ri.make_problem(spec, 2500))
     say("bit-exact rounding", state, rounds)
     st, sc, _ = run_gpu(prob, dev)
-    st_o, sc_o, _, _ = oracle.materialize(prob)
+    st_o, sc_o, ex, _ = oracle.materialize(prob, want_exact=True)
     for l in range(spec.L):
-        assert np.array_equal(st[l].view(np.uint8), st_o[l].view(np.uint8)), f"layer {l} codes differ"
+        g, o = st[l].view(np.uint8), st_o[l].view(np.uint8)
+        if not np.array_equal(g, o):
+            eb = ri.ELEM_BYTES[state]
+            bad = np.argwhere(g != o)[:8]
+            lines = []
+            for slot, byte in bad:
+                e = byte // eb
+                lines.append(f"slot {slot} elem {e} (head {e // (spec.dim * spec.dstate)}): gpu "
+                             f"{g[slot, e * eb:(e + 1) * eb].tobytes().hex()} oracle "
+                             f"{o[slot, e * eb:(e + 1) * eb].tobytes().hex()} exact {ex[l][slot, e]!r}")
+            pytest.fail(f"layer {l}: {int((g != o).sum())} bytes differ; first: " + "; ".join(lines))
         if sc is not None:
             assert np.array_equal(sc[l].view(np.uint32), sc_o[l].view(np.uint32)), f"layer {l} scales differ"
 
