@@ -37,16 +37,34 @@ template <int DT> struct Chunk { uint32_t w[2 * Fmt<DT>::bytes]; };
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Every pointer the kernels dereference addresses global memory, but the bases
+// arrive as integers in device tables, so the compiler cannot infer it: the
+// accessors below cast to the global address space, which makes them global_*
+// instructions (flat ones would also count against the LDS wait counter).
+#define RSSM_GLOBAL __attribute__((address_space(1)))
+
 template <bool NT, typename V>
 __device__ __forceinline__ V ld(const char* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
-  else return *reinterpret_cast<const V*>(p);
+  const RSSM_GLOBAL V* g = (const RSSM_GLOBAL V*)(p);
+  if constexpr (NT) return __builtin_nontemporal_load(g);
+  else return *g;
 }
 
 template <bool NT, typename V>
 __device__ __forceinline__ void st(char* p, V v) {
-  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
-  else *reinterpret_cast<V*>(p) = v;
+  RSSM_GLOBAL V* g = (RSSM_GLOBAL V*)(p);
+  if constexpr (NT) __builtin_nontemporal_store(v, g);
+  else *g = v;
+}
+
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+  return *(const RSSM_GLOBAL T*)(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void gstore(T* p, T v) {
+  *(RSSM_GLOBAL T*)(p) = v;
 }
 
 // NT: non-temporal (streaming) access, for data read or written once.

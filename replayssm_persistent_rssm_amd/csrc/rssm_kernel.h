@@ -91,12 +91,20 @@ __device__ __forceinline__ int count_active(const int32_t* active, int B, int la
   return B;
 }
 
-// Max over the 16 lanes of an aligned lane group (one state row).
+// Value of lane-permuted v within each 16-lane DPP row (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 16 lanes of an aligned lane group (one state row): swap lane
+// pairs, then pairs of pairs (quad_perm), then mirror within 8 lanes and
+// within 16 lanes.  NaN inputs are ignored, as by fmaxf.
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 8, 16));
-  v = fmaxf(v, __shfl_xor(v, 4, 16));
-  v = fmaxf(v, __shfl_xor(v, 2, 16));
-  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));  // row_mirror
   return v;
 }
 
@@ -135,8 +143,20 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
     for (int i = 0; i < 8; ++i) t[i] = acc[i] * inv;
     if constexpr (ST == kI8) {
       uint32_t code[8];
+      bool has_nan = false;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) code[i] = i8_round(t[i], SR, u[i]);
+      for (int i = 0; i < 8; ++i) has_nan |= (t[i] != t[i]);
+      if (SR || __builtin_expect(__ballot(has_nan) != 0, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[i] = i8_round(t[i], SR, u[i]);
+      } else {
+        // Nearest-even on [-127, 127]: after the clamp, adding 1.5 * 2^23
+        // rounds to an integer in one IEEE rounding, and the low byte of the
+        // sum's bits is the two's-complement code.
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          code[i] = __float_as_uint(__builtin_amdgcn_fmed3f(t[i], -127.0f, 127.0f) + 12582912.0f) & 0xFFu;
+      }
       out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
       out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
     } else {
@@ -323,7 +343,7 @@ __global__ void __launch_bounds__(kBlock, (kWavesPerSimd<KMAX, ST>)) materialize
             if (kFull || r < DIM) {
               store_chunk<ST, NTS>(at(dst_tile + (p0 + q) * PS, lane_off), c[q]);
               if constexpr (Q) {
-                if (cc == 0) dst_scale[h * DIM + r] = src_scale[h * DIM + r];
+                if (cc == 0) gstore(dst_scale + h * DIM + r, gload(src_scale + h * DIM + r));
               }
             }
           }
@@ -371,15 +391,15 @@ __global__ void __launch_bounds__(kBlock, (kWavesPerSimd<KMAX, ST>)) materialize
           const int r = rr + p * RPP;
           if (kFull || r < DIM) {
             buf[p] = load_chunk<ST, NTL>(at(src_tile + p * PS, lane_off));
-            if constexpr (Q) sbuf[p] = src_sc[r];
+            if constexpr (Q) sbuf[p] = gload(src_sc + r);
           }
         }
 
         // Decay scan: lane j < k holds a_j; suffix products give D and w_j.
-        const float A_h = A[h];
+        const float A_h = gload(A + h);
         float dtj = 0.0f, aj = 1.0f;
         if (lane < k) {
-          dtj = dt_slot[static_cast<int64_t>(e_lane) * a.H + h];
+          dtj = gload(dt_slot + static_cast<int64_t>(e_lane) * a.H + h);
           aj = expf(dtj * A_h);
         }
         float P = aj;  // inclusive suffix product over lanes j..15
@@ -434,7 +454,7 @@ __global__ void __launch_bounds__(kBlock, (kWavesPerSimd<KMAX, ST>)) materialize
               const int rn = rr + (p + PD) * RPP;
               if (kFull || rn < DIM) {
                 buf[q] = load_chunk<ST, NTL>(at(src_tile + (p + PD) * PS, lane_off));
-                if constexpr (Q) sbuf[q] = src_sc[rn];
+                if constexpr (Q) sbuf[q] = gload(src_sc + rn);
               }
             }
             const int r = rr + p * RPP;
@@ -464,7 +484,7 @@ __global__ void __launch_bounds__(kBlock, (kWavesPerSimd<KMAX, ST>)) materialize
               const Chunk<ST> out = encode_chunk<ST, SR>(acc, u, rs);
               store_chunk<ST, NTS>(at(dst_tile + p * PS, lane_off), out);
               if constexpr (Q) {
-                if (cc == 0) dst_sc[r] = rs;
+                if (cc == 0) gstore(dst_sc + r, rs);
               }
             }
           }
@@ -489,7 +509,7 @@ __global__ void __launch_bounds__(kBlock) encode_rows_kernel(const float* rows, 
   const bool ok = row < n;
   float acc[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = ok ? rows[row * DSTATE + cc * 8 + q] : 0.0f;
+  for (int q = 0; q < 8; ++q) acc[q] = ok ? gload(rows + row * DSTATE + cc * 8 + q) : 0.0f;
   uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   if constexpr (SR) {
     const uint64_t s = static_cast<uint64_t>(*rand_seed);
@@ -504,7 +524,7 @@ __global__ void __launch_bounds__(kBlock) encode_rows_kernel(const float* rows, 
   if (ok) {
     store_chunk<ST>(out_codes + (row * DSTATE + cc * 8) * SB, c);
     if constexpr (kOneByte<ST>) {
-      if (cc == 0) out_scales[row] = rs;
+      if (cc == 0) gstore(out_scales + row, rs);
     }
   }
 }
