@@ -267,6 +267,15 @@ __device__ __forceinline__ uint32_t e4m3_sr(float t, uint32_t u) {
   return sign | (a >= 0x1p-6f ? code_n : code_s);
 }
 
+// e4m3_sr for 2^-6 <= |t| < 464 only: the normal-range rule without the
+// subnormal candidate (callers check the range for the whole wave first).
+__device__ __forceinline__ uint32_t e4m3_sr_normal(float t, uint32_t u) {
+  const uint32_t bits = __float_as_uint(t);
+  const uint32_t mag = bits & 0x7FFFFFFFu;
+  const uint32_t up = (u < ((mag & 0xFFFFFu) << 12)) ? 1u : 0u;
+  return ((bits >> 24) & 0x80u) | min((mag >> 20) - 960u + up, 0x7Eu);
+}
+
 // General e4m3 rounding (any input): nearest-even or stochastic, saturating;
 // NaN keeps its sign with the NaN code.  Used where inputs are not row-scaled.
 __device__ __forceinline__ uint32_t e4m3_round(float t, bool stochastic, uint32_t u) {
