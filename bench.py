@@ -129,7 +129,22 @@ def main():
                     help="workload of the profile modes (the headline line always uses large_bf16)")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the int8 and e4m3+Philox workload lines")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM-traffic summary of two --pmc-calibrate counter runs and exit")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="print the kernel-stats table of a --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
+                    help="print the counter values of each materialize dispatch of a --pmc run and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(pmc_summary(args.summarize_pmc), end="")
+        return
+    if args.summarize_counters:
+        print(counters_summary(*args.summarize_counters), end="")
+        return
+    if args.summarize_trace:
+        print(trace_summary(args.summarize_trace), end="")
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this path needs no collectives and every run here uses a "
               "single MI355X; --gpus must be 1", file=sys.stderr)
@@ -331,6 +346,93 @@ def other_workload(name, dev, stream, steps):
     del call, tabs, dp
     torch.cuda.empty_cache()
     return out
+
+
+def _counter_rows(path, counter):
+    """(kernel name, value) per dispatch of one counter, in dispatch order."""
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = rows.get(d, (r["Kernel_Name"], 0.0))
+            rows[d] = (name, v + float(r["Counter_Value"]))
+    return [rows[d] for d in sorted(rows)]
+
+
+def counters_summary(fetch_csv, write_csv):
+    """HBM traffic of the headline kernel from FETCH_SIZE and WRITE_SIZE runs of
+    `--pmc-calibrate` (KiB per dispatch).  The run ends with two 1 GiB device
+    copies (1 GiB read and 1 GiB written each): their readings give the factor
+    from counter KiB to bytes that is applied to the materialize dispatches."""
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    out = []
+    facs = []
+    for rows, what in ((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE")):
+        copies = [v for n, v in rows if "copyBuffer" in n][-2:]
+        mats = [v for n, v in rows if "materialize_kernel" in n]
+        if len(copies) != 2 or not mats:
+            raise SystemExit(f"{what}: expected 2 calibration copies and materialize dispatches")
+        facs.append((what, copies, mats, gib_kib / (sum(copies) / 2)))
+    import rssm_inputs as ri
+    import rssm_harness as hx
+    spec = ri.CONFIGS[WORKLOAD]
+    alg = hx.algorithmic_bytes(spec, ri.make_meta(spec, np.random.default_rng(SEEDS[WORKLOAD])))
+    rd = sum(facs[0][2]) / len(facs[0][2]) * facs[0][3] * 1024
+    wr = sum(facs[1][2]) / len(facs[1][2]) * facs[1][3] * 1024
+    repo = "$REPO"
+    out.append("# HBM traffic of materialize_kernel<bf16 state, bf16 input, 64x128, kmax 8> on the large_bf16 workload")
+    out.append("# (48 layers, 256 active requests, 256 heads of 64x128 bf16; one full-batch call per dispatch)")
+    out.append("# commands (REPO = repository root on the GPU box):")
+    for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        out.append(f"#   cd /tmp && rocprofv3 --pmc {c} --output-format csv -d /tmp/pmc_{d} -o {d} -- "
+                   f"python3 {repo}/bench.py --pmc-calibrate")
+    out.append(f"#   python3 {repo}/bench.py --summarize-counters /tmp/pmc_fetch/fetch_counter_collection.csv "
+               "/tmp/pmc_write/write_counter_collection.csv")
+    out.append("# calibration: the run ends with two torch copy_ of 1 GiB (__amd_rocclr_copyBuffer: 1 GiB read, "
+               "1 GiB written)")
+    for what, copies, mats, fac in facs:
+        out.append(f"#   {what} per copy: {copies[0]:.1f}, {copies[1]:.1f} KiB -> factor {fac:.4f}")
+    out.append("# materialize dispatches: FETCH_SIZE " + ", ".join(f"{v:.1f}" for v in facs[0][2])
+               + " KiB; WRITE_SIZE " + ", ".join(f"{v:.1f}" for v in facs[1][2]) + " KiB")
+    out.append(f"kernel_source_hash: {kernel_hash()}")
+    out.append(f"fetch_factor: {facs[0][3]:.4f}")
+    out.append(f"write_factor: {facs[1][3]:.4f}")
+    out.append(f"hbm_read_bytes_per_launch: {rd:.0f}")
+    out.append(f"hbm_write_bytes_per_launch: {wr:.0f}")
+    out.append(f"hbm_bytes_per_launch: {rd + wr:.0f}")
+    out.append(f"algorithmic_bytes_per_launch: {alg}")
+    out.append(f"traffic_over_algorithmic: {(rd + wr) / alg:.4f}")
+    return "\n".join(out) + "\n"
+
+
+def pmc_summary(path):
+    """One line per materialize dispatch: dispatch id, then counter=value."""
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if "materialize_kernel" not in r["Kernel_Name"]:
+                continue
+            d = rows.setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return "".join(f"dispatch {d}: " + " ".join(f"{k}={v:.6g}" for k, v in sorted(c.items())) + "\n"
+                   for d, c in sorted(rows.items()))
+
+
+def trace_summary(stats_csv):
+    """Rows of rocprofv3's kernel_stats.csv: name | calls | average | min | max | total | percent (ns)."""
+    import csv
+    out = ["# rocprofv3 kernel stats (ns): name | calls | average | min | max | total | percent"]
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            out.append(f"{r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
+                       f"{float(r['MaxNs']):.0f} | {float(r['TotalDurationNs']):.0f} | {float(r['Percentage']):.2f}")
+    return "\n".join(out) + "\n"
 
 
 if __name__ == "__main__":
