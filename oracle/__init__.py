@@ -134,29 +134,37 @@ def materialize(prob, want_exact: bool = False, state_dtype: Optional[str] = Non
     (and scale) pools with the destination tiles written, and -- when
     ``want_exact`` -- per-layer fp64 pools holding the unrounded result and the
     magnitude sum of every written element (NaN elsewhere)."""
+    return materialize_checkpoints(prob, [prob.meta.dst], [prob.meta.prefix], want_exact,
+                                   state_dtype, philox_rounds, seed)
+
+
+def materialize_checkpoints(prob, dst_list, prefix_list, want_exact: bool = False,
+                            state_dtype: Optional[str] = None, philox_rounds: Optional[int] = None,
+                            seed: Optional[int] = None):
+    """Several checkpoints per request in one operation: checkpoint c writes,
+    for every selected (layer, request), the state after prefix_list[c][b]
+    ring entries to slot dst_list[c][l, b].  By definition each checkpoint is
+    the single-checkpoint materialize with that destination table and prefix
+    table, and every checkpoint reads the state and ring as they were before
+    the operation -- so a destination may be the request's own source slot (an
+    in-place flush: the pull-request page's "flush" of the buffered tokens into
+    the state), and a checkpoint whose destination is the pad slot is skipped
+    on its own.  The ring-buffer scheme of the flashinfer pages keeps several
+    states per request (the gated-delta-rule commit page's track_steps writes
+    an extra checkpoint next to the in-place commit).
+
+    Returns (state_out, scale_out, exact, mag) as ``materialize``."""
     spec, meta = prob.spec, prob.meta
+    if len(dst_list) != len(prefix_list) or not dst_list:
+        raise ValueError("one prefix table per destination table, at least one")
     sdt = state_dtype or spec.state_dtype
     p = params(spec, sdt, philox_rounds, seed)
     src_arr = np.ascontiguousarray(meta.src, np.int32)
-    dst_arr = np.ascontiguousarray(meta.dst, np.int32)
     rs = np.ascontiguousarray(meta.ring_start, np.int32)
-    pf = np.ascontiguousarray(meta.prefix, np.int32)
     ac = np.ascontiguousarray(meta.active, np.int32)
-    state_in = [np.ascontiguousarray(s) for s in prob.state]
-    scale_in = [np.ascontiguousarray(s) for s in prob.scale] if prob.scale else None
-    keep = [state_in, scale_in, prob.x, prob.Bm, prob.dt, prob.A]
-    ins = _Inputs(state=_ptr_array(state_in), state_stride=_i64(meta.state_stride),
-                  scale=_ptr_array(scale_in) if scale_in else None,
-                  scale_stride=_i64(meta.scale_stride),
-                  x=_ptr_array(prob.x), x_stride=_i64(meta.x_stride),
-                  Bm=_ptr_array(prob.Bm), B_stride=_i64(meta.B_stride),
-                  dt=_ptr_array(prob.dt), dt_stride=_i64(meta.dt_stride),
-                  A=_ptr_array(prob.A),
-                  src_slots=src_arr.ctypes.data_as(_P(ctypes.c_int32)),
-                  dst_slots=dst_arr.ctypes.data_as(_P(ctypes.c_int32)),
-                  ring_start=rs.ctypes.data_as(_P(ctypes.c_int32)),
-                  prefix_len=pf.ctypes.data_as(_P(ctypes.c_int32)),
-                  active=ac.ctypes.data_as(_P(ctypes.c_int32)))
+    # the pre-call snapshot every checkpoint reads
+    state_in = [np.ascontiguousarray(s).copy() for s in prob.state]
+    scale_in = [np.ascontiguousarray(s).copy() for s in prob.scale] if prob.scale else None
     state_out = [s.copy() for s in state_in]
     scale_out = [s.copy() for s in scale_in] if scale_in else None
     exact = mag = None
@@ -167,10 +175,28 @@ def materialize(prob, want_exact: bool = False, state_dtype: Optional[str] = Non
                     scale=_ptr_array(scale_out) if scale_out else None,
                     exact=_ptr_array(exact) if exact else None,
                     mag=_ptr_array(mag) if mag else None)
-    st = lib().orc_materialize(ctypes.byref(p), ctypes.byref(ins), ctypes.byref(outs))
-    del keep
-    if st != 0:
-        raise OracleError(f"orc_materialize returned {st}")
+    for dst, pref in zip(dst_list, prefix_list):
+        dst_arr = np.ascontiguousarray(dst, np.int32)
+        pf = np.ascontiguousarray(pref, np.int32)
+        if dst_arr.shape != src_arr.shape or pf.shape != rs.shape:
+            raise ValueError("destination tables are (L, B), prefix tables (B,)")
+        keep = [state_in, scale_in, prob.x, prob.Bm, prob.dt, prob.A, dst_arr, pf]
+        ins = _Inputs(state=_ptr_array(state_in), state_stride=_i64(meta.state_stride),
+                      scale=_ptr_array(scale_in) if scale_in else None,
+                      scale_stride=_i64(meta.scale_stride),
+                      x=_ptr_array(prob.x), x_stride=_i64(meta.x_stride),
+                      Bm=_ptr_array(prob.Bm), B_stride=_i64(meta.B_stride),
+                      dt=_ptr_array(prob.dt), dt_stride=_i64(meta.dt_stride),
+                      A=_ptr_array(prob.A),
+                      src_slots=src_arr.ctypes.data_as(_P(ctypes.c_int32)),
+                      dst_slots=dst_arr.ctypes.data_as(_P(ctypes.c_int32)),
+                      ring_start=rs.ctypes.data_as(_P(ctypes.c_int32)),
+                      prefix_len=pf.ctypes.data_as(_P(ctypes.c_int32)),
+                      active=ac.ctypes.data_as(_P(ctypes.c_int32)))
+        st = lib().orc_materialize(ctypes.byref(p), ctypes.byref(ins), ctypes.byref(outs))
+        del keep
+        if st != 0:
+            raise OracleError(f"orc_materialize returned {st}")
     return state_out, scale_out, exact, mag
 
 

@@ -200,6 +200,45 @@ def make_meta(spec: Spec, rng: np.random.Generator, n_active: Optional[int] = No
 # --------------------------------------------------------------------------
 # Host problems (numpy)
 # --------------------------------------------------------------------------
+def make_checkpoints(spec: Spec, meta: Meta, seed: int, n_ck: int, in_place: bool = False,
+                     k0_frac: float = 0.0, pad_frac: float = 0.0, dup_frac: float = 0.0):
+    """Destination and prefix tables of n_ck checkpoints per request:
+    dst (n_ck, L, B) int32 and prefix (n_ck, B) int32.
+
+    Checkpoint 0 is the problem's own (dst, prefix) -- or, with `in_place`,
+    the source slot itself.  The others take distinct slots that neither the
+    source nor the destination table uses, and prefix lengths ~ U[0, W];
+    `k0_frac` forces some to 0, `dup_frac` copies checkpoint 0's length, and
+    `pad_frac` replaces some destinations of checkpoints >= 1 with the pad
+    slot.  Needs enough free slots: spec.slots >= (n_ck + 1) * B."""
+    rng = np.random.default_rng(seed)
+    L, B, pad = spec.L, spec.B, spec.pad_slot_id
+    dst = np.empty((n_ck, L, B), np.int32)
+    pre = np.empty((n_ck, B), np.int32)
+    dst[0] = np.where(meta.src == pad, pad, meta.src) if in_place else meta.dst
+    pre[0] = meta.prefix
+    for c in range(1, n_ck):
+        pre[c] = rng.integers(0, spec.W + 1, size=B)
+        if k0_frac > 0:
+            pre[c, rng.permutation(B)[:int(round(k0_frac * B))]] = 0
+        if dup_frac > 0:
+            sel = rng.permutation(B)[:int(round(dup_frac * B))]
+            pre[c, sel] = pre[0, sel]
+    for l in range(L):
+        used = set(int(v) for v in meta.src[l]) | set(int(v) for v in meta.dst[l])
+        free = np.array([v for v in rng.permutation(meta.slots) if int(v) not in used and int(v) != pad], np.int32)
+        need = (n_ck - 1) * B
+        if len(free) < need:
+            raise ValueError(f"{n_ck} checkpoints need {need} free slots per layer, the pool has {len(free)}")
+        for c in range(1, n_ck):
+            dst[c, l] = free[(c - 1) * B:c * B]
+        if pad_frac > 0 and n_ck > 1:
+            npad = int(round(pad_frac * B))
+            for c in range(1, n_ck):
+                dst[c, l, rng.permutation(B)[:npad]] = pad
+    return dst, pre
+
+
 @dataclasses.dataclass
 class Problem:
     spec: Spec
