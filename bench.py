@@ -127,6 +127,8 @@ def main():
                     help="counter mode: 2 full-batch calls, then 2 plain device copies of 1 GiB")
     ap.add_argument("--workload", default=WORKLOAD, choices=["large_bf16", "large_i8", "large_f8sr"],
                     help="workload of the profile modes (the headline line always uses large_bf16)")
+    ap.add_argument("--no-checkpoints", action="store_true",
+                    help="skip the multi-checkpoint (flush + checkpoint) line")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the int8 and e4m3+Philox workload lines")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -310,12 +312,55 @@ def main():
         say(f"CPU oracle sample (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(dp, args.cpu_seconds)
 
+    if not args.no_checkpoints:
+        result["checkpoints"] = checkpoint_workload(dp, tabs, spec, stream, max(4, args.steps // 2))
+
     if not args.no_other_workloads:
         del call, tabs, dp
         torch.cuda.empty_cache()
         result["other_workloads"] = {name: other_workload(name, dev, stream, max(5, args.steps // 2))
                                      for name in ("large_i8", "large_f8sr")}
     print(json.dumps(result), flush=True)
+
+
+def checkpoint_workload(dp, tabs, spec, stream, steps):
+    """The large_bf16 problem with two checkpoints per request: every buffered
+    token flushed in place plus the state at half the prefix written to the
+    request's destination slot -- one multi-checkpoint call, against the same
+    two results from two single-checkpoint calls (checkpoint first, then the
+    in-place flush).  The flush rewrites the sources, so timed calls keep
+    evolving the state (values stay bounded: every token decays it)."""
+    import torch
+    import rssm_harness as hx
+    dev = dp.state[0].device
+    dst, pre = hx.flush_and_checkpoint_tables(dp.meta)
+    t_dst = torch.from_numpy(dst).to(dev)
+    t_pre = torch.from_numpy(pre).to(dev)
+    multi = hx.prepared_checkpoints(dp, tabs, t_dst, t_pre)
+    half = hx.prepared(dp, tabs, replay_prefix_len=t_pre[1])      # writes dst slots
+    flush_tabs = hx.Tables(**{**tabs.__dict__, "dst_slots": t_dst[0]})
+    flush = hx.prepared(dp, flush_tabs)                              # dst = src
+    for _ in range(2):
+        multi()
+    torch.cuda.synchronize()
+    ms_multi = timed_calls(multi, steps, stream)
+
+    def two():
+        half()
+        flush()
+    two()
+    torch.cuda.synchronize()
+    ms_two = timed_calls(two, steps, stream)
+    nbytes = hx.checkpoint_bytes(spec, dp.meta, dst, pre)
+    out = {"workload": "large_bf16 with 2 checkpoints per request: in-place flush of all k tokens + the state "
+                       "after k//2 tokens in the destination slot",
+           "ms_per_call": round(ms_multi, 4), "algorithmic_bytes": nbytes,
+           "GB/s": round(nbytes / (ms_multi * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(nbytes / (ms_multi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "two_single_calls_ms": round(ms_two, 4),
+           "speedup_vs_two_calls": round(ms_two / ms_multi, 3)}
+    say(f"checkpoints: {out}")
+    return out
 
 
 def other_workload(name, dev, stream, steps):

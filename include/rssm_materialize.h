@@ -101,9 +101,13 @@ typedef struct {
  *
  * Device-metadata contract (not checked, as on the page): ring_start in
  * [0, R) and replay_prefix_len in [0, max_window] for selected requests;
- * slots in range of their pools; destinations disjoint from every source
- * and from each other; bases 16-byte aligned and slot strides times element
- * size multiples of 16 bytes.  Violations are undefined behaviour; as a
+ * slots in range of their pools; destinations disjoint from every other
+ * request's source and from each other; bases 16-byte aligned and slot
+ * strides times element size multiples of 16 bytes.  A destination may be
+ * the request's own source slot in that layer (an in-place flush of the
+ * buffered tokens into the state, the "flush" of the pull-request page's
+ * Description): each state element and row scale is read before it is
+ * written, by the same wavefront.  Violations are undefined behaviour; as a
  * guard against faults the kernel clamps the prefix length to
  * [0, max_window], reduces ring_start modulo R and skips negative slots. */
 typedef struct {
@@ -131,6 +135,40 @@ typedef struct {
 rssm_status rssm_materialize(const rssm_materialize_desc *desc,
                              const rssm_materialize_tables *tables,
                              void *hip_stream);
+
+/* Most checkpoints per request of rssm_materialize_checkpoints. */
+#define RSSM_MAX_CHECKPOINTS 4
+
+/* Several checkpoints per request from one read of each source tile.  The
+ * ring-buffer scheme of the flashinfer pages keeps more than one state per
+ * request: a prefix cache that saves every `period` tokens needs the state at
+ * a period boundary while the serving loop also flushes all buffered tokens
+ * (the pull-request page's Description and the materialize page's Notes), and
+ * the gated-delta-rule commit page writes an extra tracked checkpoint next to
+ * its in-place commit (track_state_indices / track_steps).
+ *
+ * tables->dst_slots points to num_checkpoints consecutive [L][B] int32
+ * tables and tables->replay_prefix_len to num_checkpoints consecutive [B]
+ * int32 arrays; every other field is as for rssm_materialize.  The result is
+ * that of num_checkpoints rssm_materialize calls, call c with destination
+ * table c and prefix table c, all reading the state as it was before this
+ * call: checkpoint c of request b in layer l is skipped when its destination
+ * is pad_slot_id (the others are not), all are skipped when the source is;
+ * a zero prefix copies bytes.  Prefix lengths may come in any order and may
+ * repeat.  Destinations of one request are distinct; one of them may be the
+ * source slot (in-place flush).
+ *
+ * Numerics: the fold runs once over the longest prefix and stores the fp32
+ * running state at each shorter prefix, so the shortest positive checkpoint
+ * is bit-identical to a rssm_materialize call with that prefix and the
+ * others differ from separate calls only by fp32 rounding order; stochastic
+ * rounding draws the same words as separate calls.  Compiled for
+ * (dim, dstate) = (64, 128).  num_checkpoints outside
+ * [1, RSSM_MAX_CHECKPOINTS] returns RSSM_ERR_INVALID_ARGUMENT; 1 is
+ * exactly rssm_materialize. */
+rssm_status rssm_materialize_checkpoints(const rssm_materialize_desc *desc,
+                                         const rssm_materialize_tables *tables,
+                                         int32_t num_checkpoints, void *hip_stream);
 
 /* Text of the last non-OK status returned on the calling thread ("" if none).
  * The pointer stays valid until the next call on that thread. */

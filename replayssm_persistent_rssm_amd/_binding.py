@@ -17,7 +17,9 @@ LIB_PATH = os.path.join(_PKG, "librssm_materialize.so")
 
 RSSM_F32, RSSM_BF16, RSSM_F16, RSSM_I8, RSSM_F8E4M3 = 0, 1, 2, 3, 4
 RSSM_OK, RSSM_ERR_INVALID_ARGUMENT, RSSM_ERR_UNSUPPORTED, RSSM_ERR_HIP = 0, 1, 2, 3
-EXPORTS = ("rssm_materialize", "rssm_last_error", "rssm_materialize_launch_config", "rssm_debug_encode_rows")
+EXPORTS = ("rssm_materialize", "rssm_materialize_checkpoints", "rssm_last_error", "rssm_materialize_launch_config",
+           "rssm_debug_encode_rows")
+RSSM_MAX_CHECKPOINTS = 4
 _INT32_MAX = 2**31 - 1
 
 
@@ -55,6 +57,9 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     lib.rssm_materialize.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(RssmTables), ctypes.c_void_p]
     lib.rssm_materialize.restype = ctypes.c_int
+    lib.rssm_materialize_checkpoints.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(RssmTables),
+                                                 ctypes.c_int32, ctypes.c_void_p]
+    lib.rssm_materialize_checkpoints.restype = ctypes.c_int
     lib.rssm_last_error.argtypes = []
     lib.rssm_last_error.restype = ctypes.c_char_p
     lib.rssm_materialize_launch_config.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(ctypes.c_int32),
@@ -156,11 +161,14 @@ def _marshal(state_ptrs, state_slot_strides, x_cache_ptrs, x_cache_slot_strides,
              state_scale_slot_strides, src_slots, dst_slots, ring_start, replay_prefix_len,
              active_request_indices, *, state_dtype, input_dtype, matrixA_dtype, dim: int, dstate: int,
              num_heads: int, heads_per_group: int, max_window: int, ring_buffer_len: int, pad_slot_id: int = -1,
-             rand_seed=None, philox_rounds: int = 0, max_workgroups: int = 0):
-    """Check host-visible tensor metadata and build the C descriptor and tables."""
+             rand_seed=None, philox_rounds: int = 0, max_workgroups: int = 0, num_checkpoints=None):
+    """Check host-visible tensor metadata and build the C descriptor and tables.
+    num_checkpoints=None: dst_slots (L, B) and replay_prefix_len (B,); else
+    (C, L, B) and (C, B)."""
     import torch
     L = int(state_ptrs.shape[0])
     Bsz = int(ring_start.shape[0])
+    C = () if num_checkpoints is None else (int(num_checkpoints),)
     desc = make_desc(num_layers=L, batch=Bsz, num_heads=num_heads, heads_per_group=heads_per_group, dim=dim,
                      dstate=dstate, max_window=max_window, ring_buffer_len=ring_buffer_len,
                      state_dtype=state_dtype, input_dtype=input_dtype, matrixA_dtype=matrixA_dtype,
@@ -182,9 +190,9 @@ def _marshal(state_ptrs, state_slot_strides, x_cache_ptrs, x_cache_slot_strides,
         scale_slot_strides=_ptr(state_scale_slot_strides, "state_scale_slot_strides", i64, (L,))
         if quant or state_scale_slot_strides is not None else None,
         src_slots=_ptr(src_slots, "src_slots", i32, (L, Bsz)),
-        dst_slots=_ptr(dst_slots, "dst_slots", i32, (L, Bsz)),
+        dst_slots=_ptr(dst_slots, "dst_slots", i32, C + (L, Bsz)),
         ring_start=_ptr(ring_start, "ring_start", i32, (Bsz,)),
-        replay_prefix_len=_ptr(replay_prefix_len, "replay_prefix_len", i32, (Bsz,)),
+        replay_prefix_len=_ptr(replay_prefix_len, "replay_prefix_len", i32, C + (Bsz,)),
         active_request_indices=_ptr(active_request_indices, "active_request_indices", i32, (Bsz,)),
         rand_seed=_ptr(rand_seed, "rand_seed", i64, (1,)) if rand_seed is not None else None)
     return desc, tab
@@ -214,29 +222,54 @@ def rssm_materialize(*args, stream=None, **kw) -> None:
 replayssm_materialize = rssm_materialize
 
 
+def _num_checkpoints(dst_slots) -> int:
+    if getattr(dst_slots, "dim", lambda: 0)() != 3:
+        raise ValueError("dst_slots of a multi-checkpoint call has shape (num_checkpoints, L, B)")
+    return int(dst_slots.shape[0])
+
+
+def rssm_materialize_checkpoints(*args, stream=None, **kw) -> None:
+    """Enqueue one multi-checkpoint call: the arguments of rssm_materialize,
+    except that dst_slots is a device int32 (C, L, B) tensor and
+    replay_prefix_len a device int32 (C, B) tensor, C in [1, 4] checkpoints
+    per request (C is dst_slots.shape[0])."""
+    C = _num_checkpoints(args[12] if len(args) > 12 else kw["dst_slots"])
+    desc, tab = _marshal(*args, num_checkpoints=C, **kw)
+    _check(_lib.rssm_materialize_checkpoints(ctypes.byref(desc), ctypes.byref(tab), C, _stream_handle(stream)))
+
+
 class MaterializeCall:
-    """A prepared rssm_materialize: the arguments are checked and marshalled
+    """A prepared rssm_materialize (or, with checkpoints=True,
+    rssm_materialize_checkpoints): the arguments are checked and marshalled
     once, and each call is one C call with the stored descriptor and tables.
 
-    Same arguments as rssm_materialize; stream=None binds torch's current
+    Same arguments as the entry point; stream=None binds torch's current
     stream at construction.  The caller keeps every tensor alive while the
     object is used.  A call may pass another device int32 tensor of shape
     (B,) as the active list."""
 
-    def __init__(self, *args, stream=None, **kw):
-        self._desc, self._tab = _marshal(*args, **kw)
+    def __init__(self, *args, stream=None, checkpoints: bool = False, **kw):
+        self._ncp = None
+        if checkpoints:
+            self._ncp = _num_checkpoints(args[12] if len(args) > 12 else kw["dst_slots"])
+        self._desc, self._tab = _marshal(*args, num_checkpoints=self._ncp, **kw)
         self._desc_ref = ctypes.byref(self._desc)
         self._tab_ref = ctypes.byref(self._tab)
         self._stream = _stream_handle(stream)
         self._batch = int(self._desc.batch)
-        self._fn = _lib.rssm_materialize
+        if self._ncp is None:
+            fn = _lib.rssm_materialize
+            self._call = lambda: fn(self._desc_ref, self._tab_ref, self._stream)
+        else:
+            fn, ncp = _lib.rssm_materialize_checkpoints, self._ncp
+            self._call = lambda: fn(self._desc_ref, self._tab_ref, ncp, self._stream)
 
     def __call__(self, active_request_indices=None) -> None:
         if active_request_indices is not None:
             import torch
             self._tab.active_request_indices = _ptr(active_request_indices, "active_request_indices",
                                                     torch.int32, (self._batch,))
-        st = self._fn(self._desc_ref, self._tab_ref, self._stream)
+        st = self._call()
         if st != RSSM_OK:
             raise RssmError(st, rssm_last_error())
 

@@ -34,6 +34,7 @@
 namespace rssm {
 
 constexpr int kWaves = 4;             // wavefronts per workgroup
+constexpr int kMaxCheckpoints = 4;    // checkpoints per request of the multi-checkpoint instances
 constexpr int kBlock = 64 * kWaves;   // threads per workgroup
 
 struct KernelArgs {
@@ -55,6 +56,7 @@ struct KernelArgs {
   const int32_t* active;
   const int64_t* rand_seed;
   int32_t L, B, H, hpg, R, W, pad, rounds;
+  int32_t ncp;  // checkpoints per request (1 for the single-checkpoint operation)
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -245,7 +247,34 @@ constexpr int waves_per_simd() {
   return Tune::kWavesPerSimd > 0 ? Tune::kWavesPerSimd : kWavesPerSimd<KMAX, ST>;
 }
 
-template <int ST, int IT, int DIM, int DSTATE, int KMAX, bool SR, class Tune = DefaultTune>
+// Checkpoint bookkeeping of one (request, layer): kc[c] is the prefix length of
+// the c-th checkpoint in ascending order (-1: skipped, its destination is the
+// pad slot or it is not requested), dc[c] its destination slot.
+template <int NCK>
+__device__ __forceinline__ void sort_checkpoints(int (&kc)[NCK], int (&dc)[NCK]) {
+#pragma unroll
+  for (int i = 0; i < NCK; ++i) {
+#pragma unroll
+    for (int j = 0; j + 1 < NCK - i; ++j) {
+      const bool sw = kc[j] > kc[j + 1];
+      const int k0 = kc[j], d0 = dc[j];
+      kc[j] = sw ? kc[j + 1] : k0;
+      dc[j] = sw ? dc[j + 1] : d0;
+      kc[j + 1] = sw ? k0 : kc[j + 1];
+      dc[j + 1] = sw ? d0 : dc[j + 1];
+    }
+  }
+}
+
+// NCK = 1: the operation of the materialize page.  NCK > 1: up to NCK
+// checkpoints per request from one read of each source tile -- checkpoint c
+// writes the state after prefix_len[c][b] ring entries to slot
+// dst_slots[c][l][b].  The fold runs once over the longest prefix; the
+// tokens between consecutive checkpoint lengths form segments, and after each
+// segment the running fp32 state is encoded and stored.  Weights are
+// relative to the end of their segment: over segment [k', k''),
+// S_k'' = (prod_{k'<=u<k''} a_u) S_k' + sum_{k'<=j<k''} dt_j (prod_{j<u<k''} a_u) x_j B_j^T.
+template <int ST, int IT, int DIM, int DSTATE, int KMAX, bool SR, int NCK = 1, class Tune = DefaultTune>
 __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) materialize_kernel(const KernelArgs a) {
   constexpr int TPR = DSTATE / 8;                 // lanes per state row
   constexpr int RPP = 64 / TPR;                   // rows per pass of a wavefront
@@ -261,9 +290,11 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
   constexpr int64_t kTile = static_cast<int64_t>(DIM) * DSTATE;
   constexpr int XCH = DIM / 8;                    // 8-row chunks of one x row
   constexpr bool Q = kOneByte<ST>;
+  constexpr bool MULTI = NCK > 1;
   static_assert(DSTATE % 8 == 0 && 64 % TPR == 0 && DIM % 8 == 0, "unsupported tile shape");
   static_assert(!Q || TPR == 16, "one-byte state needs 16 lanes per row");
   static_assert(KMAX % 4 == 0 && KMAX <= 16, "KMAX");
+  static_assert(NCK >= 1 && NCK <= 4, "NCK");
 
   __shared__ __attribute__((aligned(16))) float lds_wx[kWaves][DIM * KMAX];
 
@@ -301,6 +332,7 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
     key1 = static_cast<uint32_t>(uniform(static_cast<int>(sd >> 32)));
   }
   const int G = a.H / a.hpg;
+  const int64_t LB = static_cast<int64_t>(a.L) * a.B;
 
   for (;;) {
     if (it >= end) {
@@ -321,30 +353,57 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
     const int b = uniform(a.active[i]);
     const int64_t lb = static_cast<int64_t>(l) * a.B + b;
     const int s = uniform(a.src_slots[lb]);
-    const int d = uniform(a.dst_slots[lb]);
-    if (s == a.pad || d == a.pad || s < 0 || d < 0) continue;  // pad slot: skipped
-    const int k = min(max(uniform(a.prefix_len[b]), 0), a.W);
+    // kc/dc: checkpoints in ascending prefix order (one entry when NCK = 1).
+    int kc[NCK], dc[NCK];
+    if constexpr (!MULTI) {
+      const int d = uniform(a.dst_slots[lb]);
+      if (s == a.pad || d == a.pad || s < 0 || d < 0) continue;  // pad slot: skipped
+      kc[0] = min(max(uniform(a.prefix_len[b]), 0), a.W);
+      dc[0] = d;
+    } else {
+      if (s == a.pad || s < 0) continue;  // pad source: every checkpoint skipped
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        int d = a.pad, kk = -1;
+        if (c < a.ncp) {
+          d = uniform(a.dst_slots[c * LB + lb]);
+          kk = min(max(uniform(a.prefix_len[static_cast<int64_t>(c) * a.B + b]), 0), a.W);
+        }
+        const bool on = d != a.pad && d >= 0;  // a pad destination skips this checkpoint only
+        kc[c] = on ? kk : -1;
+        dc[c] = on ? d : 0;
+      }
+      sort_checkpoints<NCK>(kc, dc);
+      if (kc[NCK - 1] < 0) continue;
+    }
+    const int k = kc[NCK - 1];  // longest prefix
     int r0 = uniform(a.ring_start[b]) % a.R;
     if (r0 < 0) r0 += a.R;
 
     const int64_t sbase = uniform64(a.state_ptrs[l]);
     const int64_t sstride = uniform64(a.state_strides[l]);
     const char* src_state = reinterpret_cast<const char*>(sbase) + static_cast<int64_t>(s) * sstride * SB;
-    char* dst_state = reinterpret_cast<char*>(sbase) + static_cast<int64_t>(d) * sstride * SB;
+    char* dst_state[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c)
+      dst_state[c] = reinterpret_cast<char*>(sbase) + static_cast<int64_t>(dc[c]) * sstride * SB;
     const float* src_scale = nullptr;
-    float* dst_scale = nullptr;
+    float* dst_scale[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) dst_scale[c] = nullptr;
     if constexpr (Q) {
       const int64_t cbase = uniform64(a.scale_ptrs[l]);
       const int64_t cstride = uniform64(a.scale_strides[l]);
       src_scale = reinterpret_cast<const float*>(cbase) + static_cast<int64_t>(s) * cstride;
-      dst_scale = reinterpret_cast<float*>(cbase) + static_cast<int64_t>(d) * cstride;
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) dst_scale[c] = reinterpret_cast<float*>(cbase) + static_cast<int64_t>(dc[c]) * cstride;
     }
 
     if (k == 0) {
-      // Zero prefix: exact byte copy of each tile (and its row scales).
+      // Zero prefix: exact byte copy of each tile (and its row scales) to
+      // every live destination.
       for (int h = h0; h < h1; ++h) {
         const char* src_tile = src_state + h * kTile * SB;
-        char* dst_tile = dst_state + h * kTile * SB;
 #pragma unroll 1
         for (int p0 = 0; p0 < NPASS; p0 += PD) {
           Chunk<ST> c[PD];
@@ -357,9 +416,18 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
           for (int q = 0; q < PD; ++q) {
             const int r = rr + (p0 + q) * RPP;
             if (kFull || r < DIM) {
-              store_chunk<ST, NTS>(at(dst_tile + (p0 + q) * PS, lane_off), c[q]);
+              float sc = 0.0f;
               if constexpr (Q) {
-                if (cc == 0) gstore(dst_scale + h * DIM + r, gload(src_scale + h * DIM + r));
+                if (cc == 0) sc = gload(src_scale + h * DIM + r);
+              }
+#pragma unroll
+              for (int ck = 0; ck < NCK; ++ck) {
+                if (kc[ck] == 0) {
+                  store_chunk<ST, NTS>(at(dst_state[ck] + h * kTile * SB + (p0 + q) * PS, lane_off), c[q]);
+                  if constexpr (Q) {
+                    if (cc == 0) gstore(dst_scale[ck] + h * DIM + r, sc);
+                  }
+                }
               }
             }
           }
@@ -376,6 +444,17 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
                            static_cast<int64_t>(s) * uniform64(a.dt_strides[l]);
     const float* A = reinterpret_cast<const float*>(uniform64(a.A_ptrs[l]));
     const int e_lane = (r0 + lane) % a.R;  // ring entry of token `lane`
+    // End of the segment that holds token `lane` (the shortest checkpoint
+    // prefix above it); lanes at or past k hold no token.
+    int seg_end = 16;
+    if constexpr (MULTI) {
+      if (lane < k) {
+        seg_end = k;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c)
+          if (kc[c] > lane && kc[c] < seg_end) seg_end = kc[c];
+      }
+    }
 
     for (int g = h0 / a.hpg; g * a.hpg < h1; ++g) {
       // B_j for this lane's 8 columns, shared by the heads of group g.
@@ -395,9 +474,7 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
       const int he = min(h1, (g + 1) * a.hpg);
       for (int h = hb; h < he; ++h) {
         const char* src_tile = src_state + h * kTile * SB;
-        char* dst_tile = dst_state + h * kTile * SB;
         const float* src_sc = Q ? src_scale + static_cast<int64_t>(h) * DIM : nullptr;
-        float* dst_sc = Q ? dst_scale + static_cast<int64_t>(h) * DIM : nullptr;
 
         // Issue the first passes of the state stream before the ring work.
         Chunk<ST> buf[PD];
@@ -411,23 +488,37 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
           }
         }
 
-        // Decay scan: lane j < k holds a_j; suffix products give D and w_j.
+        // Decay scan: lane j < k holds a_j; suffix products within each
+        // segment give the segment decays and the weights w_j.
         const float A_h = gload(A + h);
         float dtj = 0.0f, aj = 1.0f;
         if (lane < k) {
           dtj = gload(dt_slot + static_cast<int64_t>(e_lane) * a.H + h);
           aj = expf(dtj * A_h);
         }
-        float P = aj;  // inclusive suffix product over lanes j..15
+        float P = aj;  // inclusive suffix product over lanes j .. seg_end-1
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) {
           const float o = __shfl_down(P, off);
-          if (lane + off < 16) P *= o;
+          if (lane + off < seg_end) P *= o;
         }
         float Pn = __shfl_down(P, 1);
-        if (lane >= 15) Pn = 1.0f;
+        if (lane + 1 >= seg_end) Pn = 1.0f;
         const float w = dtj * Pn;
-        const float D = __shfl(P, 0);
+        // Decay of the segment that ends at kc[c] (1 when no token is new).
+        float Dseg[NCK];
+        {
+          int prev = 0;
+#pragma unroll
+          for (int c = 0; c < NCK; ++c) {
+            if (kc[c] > prev) {
+              Dseg[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P), prev));
+              prev = kc[c];
+            } else {
+              Dseg[c] = 1.0f;
+            }
+          }
+        }
 
         // Stage w_j * x_j[r] into this wave's LDS as [row][token].  Tokens
         // k..ceil4(k)-1 pad the last block of four with -0.0: with B_j = +0
@@ -475,32 +566,96 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
             }
             const int r = rr + p * RPP;
             if (kFull || r < DIM) {
+              const float* wrow = wx + r * KMAX;
+              uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
               float acc[8];
               decode_chunk<ST>(cur, acc);
-              const float d0 = Q ? cur_sc * D : D;
+              if constexpr (!MULTI) {
+                const float d0 = Q ? cur_sc * Dseg[0] : Dseg[0];
 #pragma unroll
-              for (int c = 0; c < 8; ++c) acc[c] *= d0;
-              const float* wrow = wx + r * KMAX;
+                for (int c = 0; c < 8; ++c) acc[c] *= d0;
 #pragma unroll
-              for (int jb = 0; jb < KMAX / 4; ++jb) {
-                if (jb * 4 < k) {
-                  const float4 w4 = *reinterpret_cast<const float4*>(wrow + jb * 4);
+                for (int jb = 0; jb < KMAX / 4; ++jb) {
+                  if (jb * 4 < k) {
+                    const float4 w4 = *reinterpret_cast<const float4*>(wrow + jb * 4);
 #pragma unroll
-                  for (int c = 0; c < 8; ++c) {
-                    acc[c] = fmaf(w4.x, Bv[jb * 4 + 0][c], acc[c]);
-                    acc[c] = fmaf(w4.y, Bv[jb * 4 + 1][c], acc[c]);
-                    acc[c] = fmaf(w4.z, Bv[jb * 4 + 2][c], acc[c]);
-                    acc[c] = fmaf(w4.w, Bv[jb * 4 + 3][c], acc[c]);
+                    for (int c = 0; c < 8; ++c) {
+                      acc[c] = fmaf(w4.x, Bv[jb * 4 + 0][c], acc[c]);
+                      acc[c] = fmaf(w4.y, Bv[jb * 4 + 1][c], acc[c]);
+                      acc[c] = fmaf(w4.z, Bv[jb * 4 + 2][c], acc[c]);
+                      acc[c] = fmaf(w4.w, Bv[jb * 4 + 3][c], acc[c]);
+                    }
                   }
                 }
-              }
-              uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-              if constexpr (SR) sr_words(u, r, cc * 8, DSTATE, h, b, l, key0, key1, a.rounds);
-              float rs = 0.0f;
-              const Chunk<ST> out = encode_chunk<ST, SR>(acc, u, rs);
-              store_chunk<ST, NTS>(at(dst_tile + p * PS, lane_off), out);
-              if constexpr (Q) {
-                if (cc == 0) gstore(dst_sc + r, rs);
+                if constexpr (SR) sr_words(u, r, cc * 8, DSTATE, h, b, l, key0, key1, a.rounds);
+                float rs = 0.0f;
+                const Chunk<ST> out = encode_chunk<ST, SR>(acc, u, rs);
+                store_chunk<ST, NTS>(at(dst_state[0] + h * kTile * SB + p * PS, lane_off), out);
+                if constexpr (Q) {
+                  if (cc == 0) gstore(dst_scale[0] + static_cast<int64_t>(h) * DIM + r, rs);
+                }
+              } else {
+                // One set of random words per element serves every checkpoint,
+                // as separate calls would draw the same ones.
+                if constexpr (SR) sr_words(u, r, cc * 8, DSTATE, h, b, l, key0, key1, a.rounds);
+                // Zero-prefix checkpoints take the source bytes as they are.
+#pragma unroll
+                for (int ck = 0; ck < NCK; ++ck) {
+                  if (kc[ck] == 0) {
+                    store_chunk<ST, NTS>(at(dst_state[ck] + h * kTile * SB + p * PS, lane_off), cur);
+                    if constexpr (Q) {
+                      if (cc == 0) gstore(dst_scale[ck] + static_cast<int64_t>(h) * DIM + r, cur_sc);
+                    }
+                  }
+                }
+                Chunk<ST> out{};
+                float rs = 0.0f;
+                int prev = 0;
+#pragma unroll
+                for (int ck = 0; ck < NCK; ++ck) {
+                  const int kend = kc[ck];
+                  if (kend > prev) {
+                    // Segment [prev, kend): decay, then its tokens.
+                    const float dm = (prev == 0 && Q) ? cur_sc * Dseg[ck] : Dseg[ck];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[c] *= dm;
+#pragma unroll
+                    for (int jb = 0; jb < KMAX / 4; ++jb) {
+                      const int t0 = jb * 4;
+                      if (t0 < kend && t0 + 4 > prev) {
+                        const float4 w4 = *reinterpret_cast<const float4*>(wrow + t0);
+                        if (t0 >= prev && (t0 + 4 <= kend || kend == k)) {
+                          // whole block inside (tokens past k carry -0 weights)
+#pragma unroll
+                          for (int c = 0; c < 8; ++c) {
+                            acc[c] = fmaf(w4.x, Bv[t0 + 0][c], acc[c]);
+                            acc[c] = fmaf(w4.y, Bv[t0 + 1][c], acc[c]);
+                            acc[c] = fmaf(w4.z, Bv[t0 + 2][c], acc[c]);
+                            acc[c] = fmaf(w4.w, Bv[t0 + 3][c], acc[c]);
+                          }
+                        } else {
+                          // block cut by a segment boundary: only its own tokens
+                          const float wt[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                          for (int t = 0; t < 4; ++t) {
+                            if (t0 + t >= prev && t0 + t < kend) {
+#pragma unroll
+                              for (int c = 0; c < 8; ++c) acc[c] = fmaf(wt[t], Bv[t0 + t][c], acc[c]);
+                            }
+                          }
+                        }
+                      }
+                    }
+                    out = encode_chunk<ST, SR>(acc, u, rs);
+                    prev = kend;
+                  }
+                  if (kend > 0) {
+                    store_chunk<ST, NTS>(at(dst_state[ck] + h * kTile * SB + p * PS, lane_off), out);
+                    if constexpr (Q) {
+                      if (cc == 0) gstore(dst_scale[ck] + static_cast<int64_t>(h) * DIM + r, rs);
+                    }
+                  }
+                }
               }
             }
           }
@@ -547,7 +702,7 @@ __global__ void __launch_bounds__(kBlock) encode_rows_kernel(const float* rows, 
 
 // Kernel registry entries, one table per state dtype (one translation unit each).
 struct KernelEntry {
-  int st, it, dim, dstate, kmax, sr;
+  int st, it, dim, dstate, kmax, sr, nck;  // nck: checkpoints per request the instance handles (max)
   const void* fn;
   const char* name;
 };

@@ -178,14 +178,17 @@ const Registry& registry() {
   return r;
 }
 
-const rssm::KernelEntry* find_kernel(const rssm_materialize_desc* d) {
+// nck: 1 for the single-checkpoint operation, rssm::kMaxCheckpoints for the
+// multi-checkpoint instances.
+const rssm::KernelEntry* find_kernel(const rssm_materialize_desc* d, int nck) {
   const int kmax = d->max_window <= 8 ? 8 : 16;
   const int sr = (d->philox_rounds > 0 && d->state_dtype != RSSM_F32) ? 1 : 0;
   const Registry& reg = registry();
   const int s = d->state_dtype;
   for (int i = 0; i < reg.nk[s]; ++i) {
     const rssm::KernelEntry& e = reg.k[s][i];
-    if (e.it == d->input_dtype && e.dim == d->dim && e.dstate == d->dstate && e.kmax == kmax && e.sr == sr)
+    if (e.it == d->input_dtype && e.dim == d->dim && e.dstate == d->dstate && e.kmax == kmax && e.sr == sr &&
+        e.nck == nck)
       return &e;
   }
   return nullptr;
@@ -236,6 +239,7 @@ rssm_status grid_for(const void* fn, int* grid_out) {
 struct LaunchCache {
   rssm_materialize_desc desc;
   int device = -1;
+  int nck = 0;
   const rssm::KernelEntry* kernel = nullptr;
   int grid = 0;
 };
@@ -246,42 +250,17 @@ int lds_bytes_of(const rssm_materialize_desc* d) {
   return rssm::kWaves * d->dim * kmax * static_cast<int>(sizeof(float));
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* rssm_last_error(void) { return g_err; }
-
-rssm_status rssm_materialize_launch_config(const rssm_materialize_desc* desc, int32_t* grid, int32_t* block,
-                                           int32_t* lds_bytes) {
-  g_err[0] = '\0';
-  rssm_status st = validate_desc(desc);
-  if (st != RSSM_OK) return st;
-  if (grid == nullptr || block == nullptr || lds_bytes == nullptr)
-    return fail(RSSM_ERR_INVALID_ARGUMENT, "grid, block and lds_bytes must not be NULL");
-  const rssm::KernelEntry* k = find_kernel(desc);
-  if (k == nullptr) return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance");
-  int g = 0;
-  if (desc->max_workgroups > 0) {
-    g = desc->max_workgroups;
-  } else {
-    st = grid_for(k->fn, &g);
-    if (st != RSSM_OK) return st;
-  }
-  *grid = g;
-  *block = rssm::kBlock;
-  *lds_bytes = lds_bytes_of(desc);
-  return RSSM_OK;
-}
-
-rssm_status rssm_materialize(const rssm_materialize_desc* desc, const rssm_materialize_tables* tables,
-                             void* hip_stream) {
-  g_err[0] = '\0';
+// Validate, pick the instance (cached per thread for an unchanged
+// descriptor) and enqueue one launch.  ncp = 1 takes the single-checkpoint
+// instances, ncp > 1 the multi-checkpoint ones.
+rssm_status launch(const rssm_materialize_desc* desc, const rssm_materialize_tables* tables, int ncp,
+                   void* hip_stream) {
   if (desc == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const int nck = ncp > 1 ? rssm::kMaxCheckpoints : 1;
   const rssm::KernelEntry* k = nullptr;
   int grid = 0;
   rssm_status st;
-  const bool same_desc = g_last.kernel != nullptr &&
+  const bool same_desc = g_last.kernel != nullptr && g_last.nck == nck &&
                          std::memcmp(&g_last.desc, desc, sizeof(rssm_materialize_desc)) == 0;
   // Host validation happens before any HIP call; an unchanged descriptor was
   // validated by an earlier call on this thread.
@@ -291,17 +270,17 @@ rssm_status rssm_materialize(const rssm_materialize_desc* desc, const rssm_mater
   }
   st = validate_tables(desc, tables);
   if (st != RSSM_OK) return st;
+  k = same_desc ? g_last.kernel : find_kernel(desc, nck);
+  if (k == nullptr)
+    return fail(RSSM_ERR_UNSUPPORTED, "no compiled %sinstance for state=%s input=%s dim=%d dstate=%d",
+                nck > 1 ? "multi-checkpoint " : "", dtype_name(desc->state_dtype), dtype_name(desc->input_dtype),
+                desc->dim, desc->dstate);
   int dev = 0;
   hipError_t de = hipGetDevice(&dev);
   if (de != hipSuccess) return fail(RSSM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(de));
   if (same_desc && g_last.device == dev) {
-    k = g_last.kernel;
     grid = g_last.grid;
   } else {
-    k = find_kernel(desc);
-    if (k == nullptr)
-      return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance for state=%s input=%s dim=%d dstate=%d",
-                  dtype_name(desc->state_dtype), dtype_name(desc->input_dtype), desc->dim, desc->dstate);
     grid = desc->max_workgroups;
     if (grid == 0) {
       st = grid_for(k->fn, &grid);
@@ -309,6 +288,7 @@ rssm_status rssm_materialize(const rssm_materialize_desc* desc, const rssm_mater
     }
     g_last.desc = *desc;
     g_last.device = dev;
+    g_last.nck = nck;
     g_last.kernel = k;
     g_last.grid = grid;
   }
@@ -338,14 +318,58 @@ rssm_status rssm_materialize(const rssm_materialize_desc* desc, const rssm_mater
   args.W = desc->max_window;
   args.pad = desc->pad_slot_id;
   args.rounds = desc->philox_rounds;
+  args.ncp = ncp;
   if (verbose())
-    std::fprintf(stderr, "[rssm_materialize] %s grid=%d block=%d lds=%dB L=%d B=%d H=%d\n", k->name, grid,
-                 rssm::kBlock, lds_bytes_of(desc), desc->num_layers, desc->batch, desc->num_heads);
+    std::fprintf(stderr, "[rssm_materialize] %s grid=%d block=%d lds=%dB L=%d B=%d H=%d checkpoints=%d\n", k->name,
+                 grid, rssm::kBlock, lds_bytes_of(desc), desc->num_layers, desc->batch, desc->num_heads, ncp);
   void* params[] = {&args};
   hipError_t e = hipLaunchKernel(k->fn, dim3(grid), dim3(rssm::kBlock), params, 0,
                                  static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(RSSM_ERR_HIP, "launch of %s failed: %s", k->name, hipGetErrorString(e));
   return RSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rssm_last_error(void) { return g_err; }
+
+rssm_status rssm_materialize_launch_config(const rssm_materialize_desc* desc, int32_t* grid, int32_t* block,
+                                           int32_t* lds_bytes) {
+  g_err[0] = '\0';
+  rssm_status st = validate_desc(desc);
+  if (st != RSSM_OK) return st;
+  if (grid == nullptr || block == nullptr || lds_bytes == nullptr)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "grid, block and lds_bytes must not be NULL");
+  const rssm::KernelEntry* k = find_kernel(desc, 1);
+  if (k == nullptr) return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance");
+  int g = 0;
+  if (desc->max_workgroups > 0) {
+    g = desc->max_workgroups;
+  } else {
+    st = grid_for(k->fn, &g);
+    if (st != RSSM_OK) return st;
+  }
+  *grid = g;
+  *block = rssm::kBlock;
+  *lds_bytes = lds_bytes_of(desc);
+  return RSSM_OK;
+}
+
+rssm_status rssm_materialize(const rssm_materialize_desc* desc, const rssm_materialize_tables* tables,
+                             void* hip_stream) {
+  g_err[0] = '\0';
+  return launch(desc, tables, 1, hip_stream);
+}
+
+rssm_status rssm_materialize_checkpoints(const rssm_materialize_desc* desc, const rssm_materialize_tables* tables,
+                                         int32_t num_checkpoints, void* hip_stream) {
+  g_err[0] = '\0';
+  if (num_checkpoints < 1 || num_checkpoints > RSSM_MAX_CHECKPOINTS)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "num_checkpoints must be in [1, %d] (got %d)", RSSM_MAX_CHECKPOINTS,
+                num_checkpoints);
+  return launch(desc, tables, num_checkpoints, hip_stream);
 }
 
 rssm_status rssm_debug_encode_rows(const rssm_materialize_desc* desc, const float* rows, const int32_t* coords,

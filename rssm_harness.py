@@ -142,3 +142,54 @@ def algorithmic_bytes(spec: ri.Spec, meta: ri.Meta, n_active: Optional[int] = No
                 total += 2 * spec.H * spec.dim * 4
             total += k * (spec.H * spec.dim * ib + spec.G * spec.dstate * ib + spec.H * 4)
     return total + len(layers) * spec.H * 4
+
+
+def prepared_checkpoints(dp: ri.DeviceProblem, tabs: Tables, dst, prefix, max_workgroups: int = 0, stream=None):
+    """A multi-checkpoint MaterializeCall: dst (C, L, B) and prefix (C, B)
+    device int32 tensors replace the problem's destination and prefix tables."""
+    from replayssm_persistent_rssm_amd import MaterializeCall
+    s = dp.spec
+    return MaterializeCall(
+        tabs.state_ptrs, tabs.state_slot_strides, tabs.x_cache_ptrs, tabs.x_cache_slot_strides,
+        tabs.B_cache_ptrs, tabs.B_cache_slot_strides, tabs.dt_cache_ptrs, tabs.dt_cache_slot_strides,
+        tabs.A_ptrs, tabs.state_scale_ptrs, tabs.state_scale_slot_strides, tabs.src_slots, dst,
+        tabs.ring_start, prefix, tabs.active_request_indices,
+        state_dtype=s.state_dtype, input_dtype=s.input_dtype, matrixA_dtype="f32", dim=s.dim, dstate=s.dstate,
+        num_heads=s.H, heads_per_group=s.hpg, max_window=s.W, ring_buffer_len=s.R, pad_slot_id=s.pad_slot_id,
+        rand_seed=tabs.rand_seed, philox_rounds=s.philox_rounds, max_workgroups=max_workgroups, stream=stream,
+        checkpoints=True)
+
+
+def checkpoint_bytes(spec: ri.Spec, meta: ri.Meta, dst: np.ndarray, prefix: np.ndarray) -> int:
+    """Bytes a multi-checkpoint call must move: per (layer, request) with a
+    live source and at least one live destination, the source state once (+
+    row scales), every live checkpoint's state written (+ scales), and the
+    replayed x, B and dt rows of the longest live prefix; plus A per layer."""
+    sb = ri.ELEM_BYTES[spec.state_dtype]
+    ib = ri.ELEM_BYTES[spec.input_dtype]
+    tile = spec.H * spec.dim * spec.dstate * sb + (spec.H * spec.dim * 4 if ri.one_byte(spec.state_dtype) else 0)
+    total = 0
+    layers = set()
+    n = int((meta.active >= 0).cumprod().sum())
+    for i in range(n):
+        b = int(meta.active[i])
+        for l in range(spec.L):
+            if meta.src[l, b] == spec.pad_slot_id:
+                continue
+            live = [c for c in range(dst.shape[0]) if dst[c, l, b] != spec.pad_slot_id]
+            if not live:
+                continue
+            layers.add(l)
+            k = max(int(prefix[c, b]) for c in live)
+            total += tile * (1 + len(live))
+            total += k * (spec.H * spec.dim * ib + spec.G * spec.dstate * ib + spec.H * 4)
+    return total + len(layers) * spec.H * 4
+
+
+def flush_and_checkpoint_tables(meta: ri.Meta):
+    """Two checkpoints per request: 0 applies every buffered token in place
+    (destination = source slot, the request's prefix length); 1 writes the
+    state at half that prefix to the request's destination slot."""
+    dst = np.stack([meta.src, meta.dst]).astype(np.int32)
+    pre = np.stack([meta.prefix, meta.prefix // 2]).astype(np.int32)
+    return dst, pre

@@ -126,3 +126,54 @@ def check_against_oracle(prob, gpu_state, gpu_scale, expected=None):
             assert np.array_equal(gpu_scale[l][keep].view(np.uint8), prob.scale[l][keep].view(np.uint8)), \
                 f"layer {l}: a scale slot that is not a destination changed"
     return st_o, sc_o, ex, mg
+
+
+def checkpoint_writes(prob, dst, pre):
+    """(c, l, b, src, dst_slot, k) of every checkpoint write of a call."""
+    m, s = prob.meta, prob.spec
+    out = []
+    for i in range(s.B):
+        b = int(m.active[i])
+        if b < 0 or b >= s.B:
+            break
+        for l in range(s.L):
+            src = int(m.src[l, b])
+            if src == s.pad_slot_id:
+                continue
+            for c in range(dst.shape[0]):
+                d = int(dst[c, l, b])
+                if d != s.pad_slot_id:
+                    out.append((c, l, b, src, d, int(pre[c, b])))
+    return out
+
+
+def check_checkpoints_against_oracle(prob, dst, pre, gpu_state, gpu_scale, expected=None):
+    """Full comparison of a multi-checkpoint call's pools with the oracle's."""
+    spec = prob.spec
+    st_o, sc_o, ex, mg = expected if expected is not None else oracle.materialize_checkpoints(
+        prob, list(dst), list(pre), want_exact=True)
+    n = spec.H * spec.dim * spec.dstate
+    ns = spec.H * spec.dim
+    written = [np.zeros(a.shape[0], bool) for a in prob.state]
+    for c, l, b, s, d, k in checkpoint_writes(prob, dst, pre):
+        written[l][d] = True
+        what = f"checkpoint {c} layer {l} request {b} slot {s}->{d} k={k}"
+        if k == 0:
+            assert np.array_equal(gpu_state[l][d, :n].view(np.uint8), prob.state[l][s, :n].view(np.uint8)), what
+            if gpu_scale is not None:
+                assert np.array_equal(gpu_scale[l][d, :ns].view(np.uint32), prob.scale[l][s, :ns].view(np.uint32)), what
+        else:
+            compare_tile(spec.state_dtype, gpu_state[l][d, :n], st_o[l][d, :n], ex[l][d, :n], mg[l][d, :n],
+                         gpu_scale[l][d, :ns] if gpu_scale is not None else None,
+                         sc_o[l][d, :ns] if sc_o is not None else None, what)
+        assert np.array_equal(gpu_state[l][d, n:].view(np.uint8), prob.state[l][d, n:].view(np.uint8)), what
+        if gpu_scale is not None:
+            assert np.array_equal(gpu_scale[l][d, ns:].view(np.uint8), prob.scale[l][d, ns:].view(np.uint8)), what
+    for l in range(spec.L):
+        keep = ~written[l]
+        assert np.array_equal(gpu_state[l][keep].view(np.uint8), prob.state[l][keep].view(np.uint8)), \
+            f"layer {l}: a slot that is not a destination changed"
+        if gpu_scale is not None:
+            assert np.array_equal(gpu_scale[l][keep].view(np.uint8), prob.scale[l][keep].view(np.uint8)), \
+                f"layer {l}: a scale slot that is not a destination changed"
+    return st_o, sc_o, ex, mg

@@ -137,3 +137,35 @@ def test_algorithmic_bytes_formula():
     k = meta.prefix[meta.active[:3]]
     want = sum(spec.L * (8_388_608 + int(kk) * 35_840) for kk in k) + spec.L * spec.H * 4
     assert hx.algorithmic_bytes(spec, meta) == want
+
+
+def test_checkpoints_entry_point_validation(rp):
+    d = _desc(rp)
+    t = _fake_tables(rp)
+    for n in (0, -1, 5):
+        assert rp.lib().rssm_materialize_checkpoints(ctypes.byref(d), ctypes.byref(t), n, None) == 1
+        assert "num_checkpoints" in rp.rssm_last_error()
+    # the multi-checkpoint instances cover the 64x128 tile only
+    d16 = _desc(rp, dim=16, dstate=16)
+    assert rp.lib().rssm_materialize_checkpoints(ctypes.byref(d16), ctypes.byref(t), 2, None) == 2
+    assert "multi-checkpoint" in rp.rssm_last_error()
+    assert rp.lib().rssm_materialize_checkpoints(ctypes.byref(d), None, 2, None) == 1
+    assert rp.lib().rssm_materialize_checkpoints(None, ctypes.byref(t), 2, None) == 1
+    d8 = _desc(rp, state_dtype="i8")
+    t8 = _fake_tables(rp, scale_slot_strides=None)
+    assert rp.lib().rssm_materialize_checkpoints(ctypes.byref(d8), ctypes.byref(t8), 3, None) == 1
+    assert "scale" in rp.rssm_last_error()
+
+
+def test_checkpoint_byte_count(rp):
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    spec = ri.CONFIGS["large_bf16"]
+    meta = ri.make_meta(spec, np.random.default_rng(1002))
+    dst, pre = hx.flush_and_checkpoint_tables(meta)
+    # every (layer, request) reads its state once, writes it twice and
+    # replays the longer prefix
+    tile = spec.H * spec.dim * spec.dstate * 2
+    ring = spec.H * spec.dim * 2 + spec.G * spec.dstate * 2 + spec.H * 4
+    want = sum(spec.L * (3 * tile + int(meta.prefix[b]) * ring) for b in range(spec.B)) + spec.L * spec.H * 4
+    assert hx.checkpoint_bytes(spec, meta, dst, pre) == want
