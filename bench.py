@@ -127,6 +127,8 @@ def main():
                     help="counter mode: 2 full-batch calls, then 2 plain device copies of 1 GiB")
     ap.add_argument("--workload", default=WORKLOAD, choices=["large_bf16", "large_i8", "large_f8sr"],
                     help="workload of the profile modes (the headline line always uses large_bf16)")
+    ap.add_argument("--only-checkpoints", action="store_true",
+                    help="profile mode: the multi-checkpoint line of the large_bf16 workload only")
     ap.add_argument("--no-checkpoints", action="store_true",
                     help="skip the multi-checkpoint (flush + checkpoint) line")
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -158,7 +160,7 @@ def main():
     import replayssm_persistent_rssm_amd as rp
 
     dev = torch.device("cuda:0")
-    profile_mode = args.only_main or args.empty_only or args.pmc_calibrate
+    profile_mode = args.only_main or args.empty_only or args.pmc_calibrate or args.only_checkpoints
     wl = args.workload if profile_mode else WORKLOAD
     spec = ri.CONFIGS[wl]
     say("generating", wl, "seed", SEEDS[wl])
@@ -175,6 +177,10 @@ def main():
 
     full_bytes = hx.algorithmic_bytes(spec, dp.meta)
     call = hx.prepared(dp, tabs)   # one C call per step, arguments marshalled once
+
+    if args.only_checkpoints:
+        print(json.dumps({"checkpoints": checkpoint_workload(dp, tabs, spec, stream, args.steps)}), flush=True)
+        return
 
     if args.empty_only or args.pmc_calibrate:
         if args.empty_only:
