@@ -17,6 +17,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librssm_oracle.so")
 SRC_PATH = os.path.join(_HERE, "rssm_oracle.c")
+GDN_SRC_PATH = os.path.join(_HERE, "gdn_oracle.c")
 
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3, "f8e4m3": 4, "f64": 5}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "f8e4m3": 1, "f64": 8}
@@ -27,7 +28,7 @@ STORAGE_NP = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16,
 def build(verbose: bool = False) -> str:
     """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
+           "-fPIC", "-shared", SRC_PATH, GDN_SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
@@ -62,6 +63,21 @@ class _Outputs(ctypes.Structure):
     _fields_ = [("state", _P(_VP)), ("scale", _P(_VP)), ("exact", _P(_VP)), ("mag", _P(_VP))]
 
 
+class _GdnParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_layers", "slots", "num_v_heads", "num_k_heads", "window", "batch", "dk", "dv", "use_l2norm",
+        "null_block_id", "has_track")]
+
+
+class _GdnInputs(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("state", "rawv", "rawk", "g", "beta", "state_indices", "accept_lens",
+                                    "track_state_indices", "track_steps")]
+
+
+class _GdnOutputs(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("state_out", "exact", "mag")]
+
+
 _lib = None
 
 
@@ -87,6 +103,11 @@ def lib():
         L.orc_philox4x32.argtypes = [_P(ctypes.c_uint32), _P(ctypes.c_uint32), ctypes.c_int32,
                                      _P(ctypes.c_uint32)]
         L.orc_philox4x32.restype = None
+        L.orc_gdn_commit.argtypes = [_P(_GdnParams), _P(_GdnInputs), _P(_GdnOutputs)]
+        L.orc_gdn_commit.restype = ctypes.c_int
+        L.orc_gdn_tile.argtypes = [_P(_GdnParams), _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
+                                   _VP, _VP, _VP, _VP]
+        L.orc_gdn_tile.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -259,3 +280,64 @@ def philox4x32(ctr, key, rounds: int) -> np.ndarray:
     o = (ctypes.c_uint32 * 4)()
     lib().orc_philox4x32(c, k, int(rounds), o)
     return np.array(list(o), np.uint32)
+
+
+# ---------------------------------------------------------------------------
+# Gated-delta-rule ReplaySSM commit
+# (flashinfer.gdn_decode.gated_delta_rule_replayssm_commit; see gdn_oracle.h)
+# ---------------------------------------------------------------------------
+def gdn_params(spec, batch: Optional[int] = None, has_track: bool = False) -> _GdnParams:
+    return _GdnParams(num_layers=spec.L, slots=spec.slots, num_v_heads=spec.HV, num_k_heads=spec.H,
+                      window=spec.T, batch=spec.B if batch is None else batch, dk=spec.dk, dv=spec.dv,
+                      use_l2norm=1 if spec.use_l2norm else 0, null_block_id=spec.null_block_id,
+                      has_track=1 if has_track else 0)
+
+
+def gdn_commit(prob, want_exact: bool = False):
+    """The whole commit on a host problem (``rssm_inputs.GdnProblem``).
+    Returns (state_out, exact, mag): the fp32 state pool after the commit and,
+    with ``want_exact``, fp64 pools of the unrounded result and the magnitude
+    bound of every written tile (NaN elsewhere)."""
+    spec = prob.spec
+    has_track = prob.track_state_indices is not None
+    p = gdn_params(spec, has_track=has_track)
+    arrs = dict(state=np.ascontiguousarray(prob.state, np.float32),
+                rawv=np.ascontiguousarray(prob.rawv, np.uint16), rawk=np.ascontiguousarray(prob.rawk, np.uint16),
+                g=np.ascontiguousarray(prob.g, np.float32), beta=np.ascontiguousarray(prob.beta, np.float32),
+                state_indices=np.ascontiguousarray(prob.state_indices, np.int32),
+                accept_lens=np.ascontiguousarray(prob.accept_lens, np.int32))
+    if has_track:
+        arrs["track_state_indices"] = np.ascontiguousarray(prob.track_state_indices, np.int32)
+        arrs["track_steps"] = np.ascontiguousarray(prob.track_steps, np.int32)
+    ins = _GdnInputs(**{k: v.ctypes.data for k, v in arrs.items()})
+    state_out = arrs["state"].copy()
+    exact = mag = None
+    if want_exact:
+        exact = np.full(state_out.shape, np.nan, np.float64)
+        mag = np.full(state_out.shape, np.nan, np.float64)
+    outs = _GdnOutputs(state_out=state_out.ctypes.data, exact=exact.ctypes.data if exact is not None else None,
+                       mag=mag.ctypes.data if mag is not None else None)
+    st = lib().orc_gdn_commit(ctypes.byref(p), ctypes.byref(ins), ctypes.byref(outs))
+    if st != 0:
+        raise OracleError(f"orc_gdn_commit returned {st}")
+    return state_out, exact, mag
+
+
+def gdn_tile(spec, s0, k_win, v_win, g_win, b_win, n: int, track_step: int = -1):
+    """One (layer, request, value head) tile.  Returns (final, final_mag,
+    track, track_mag) in fp64; track entries are None unless
+    0 <= track_step < n."""
+    p = gdn_params(spec)
+    a = [np.ascontiguousarray(s0, np.float32), np.ascontiguousarray(k_win, np.uint16),
+         np.ascontiguousarray(v_win, np.uint16), np.ascontiguousarray(g_win, np.float32),
+         np.ascontiguousarray(b_win, np.float32)]
+    shape = (spec.dv, spec.dk)
+    fin, finm = np.empty(shape, np.float64), np.empty(shape, np.float64)
+    trk, trkm = np.empty(shape, np.float64), np.empty(shape, np.float64)
+    st = lib().orc_gdn_tile(ctypes.byref(p), *[x.ctypes.data for x in a], int(n), int(track_step),
+                            fin.ctypes.data, finm.ctypes.data, trk.ctypes.data, trkm.ctypes.data)
+    if st != 0:
+        raise OracleError(f"orc_gdn_tile returned {st}")
+    if 0 <= track_step < n:
+        return fin, finm, trk, trkm
+    return fin, finm, None, None

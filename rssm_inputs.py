@@ -403,3 +403,137 @@ def make_device_problem(spec: Spec, seed: int, device="cuda", n_active: Optional
     return DeviceProblem(spec=spec, meta=meta, state=state, scale=scale if scale else None,
                          x=xs, Bm=Bs, dt=dts, A=As)
 
+
+
+# --------------------------------------------------------------------------
+# Gated-delta-rule ReplaySSM commit (flashinfer.gdn_decode.
+# gated_delta_rule_replayssm_commit): contiguous pools as on that page.
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class GdnSpec:
+    """Shape and structure of one commit workload."""
+    name: str
+    L: int                     # layers
+    B: int                     # requests
+    HV: int                    # value heads
+    H: int                     # key heads (divides HV)
+    T: int                     # tokens per cached window
+    slots: int                 # pool slots per layer
+    dk: int = 128
+    dv: int = 128
+    use_l2norm: bool = True
+    null_block_id: int = -1
+    null_frac: float = 0.0     # requests whose slot is <= null_block_id
+    track: bool = False
+    accept: Optional[Sequence[int]] = None   # explicit accept_lens, else U[0, T]
+    zero_frac: float = 0.0     # requests forced to accept 0
+
+
+GDN_CONFIGS = {
+    # all shapes the page fixes: fp32 128x128 K-last state, bf16 windows, T <= 8
+    "gdn_small": GdnSpec("gdn_small", L=2, B=6, HV=4, H=2, T=8, slots=16, null_frac=0.2, track=True,
+                         zero_frac=0.2),
+    # 48 layers, 256 requests, 32 value heads over 16 key heads, 8-token windows
+    "gdn_large": GdnSpec("gdn_large", L=48, B=256, HV=32, H=16, T=8, slots=512, null_frac=1 / 16, track=True,
+                         zero_frac=1 / 16),
+}
+
+
+@dataclasses.dataclass
+class GdnProblem:
+    spec: GdnSpec
+    state: np.ndarray                 # (L, slots, HV, dv, dk) fp32
+    rawv: np.ndarray                  # (L, slots, HV, T, dv) bf16 codes (uint16)
+    rawk: np.ndarray                  # (L, slots, H, T, dk) bf16 codes (uint16)
+    g: np.ndarray                     # (L, slots, HV, T) fp32 log decay
+    beta: np.ndarray                  # (L, slots, HV, T) fp32 in (0, 1)
+    state_indices: np.ndarray         # (B,) int32
+    accept_lens: np.ndarray           # (B,) int32
+    track_state_indices: Optional[np.ndarray]
+    track_steps: Optional[np.ndarray]
+
+
+def make_gdn_meta(spec: GdnSpec, rng: np.random.Generator):
+    """state_indices (distinct live slots above null_block_id, some requests
+    null), accept_lens ~ U[0, T] (some forced 0), and -- with tracking --
+    distinct track slots disjoint from the live ones and steps ~ U[-1, T-1]
+    (so some fall outside the accepted prefix)."""
+    B, nb = spec.B, spec.null_block_id
+    live_pool = np.arange(nb + 1, spec.slots)
+    need = B * (2 if spec.track else 1)
+    if len(live_pool) < need:
+        raise ValueError(f"{spec.name}: {need} slots needed above null_block_id, the pool has {len(live_pool)}")
+    perm = rng.permutation(live_pool)
+    idx = perm[:B].astype(np.int32)
+    n_null = int(round(spec.null_frac * B))
+    if n_null:
+        idx[rng.permutation(B)[:n_null]] = rng.integers(-1, nb + 1, size=n_null) if nb >= 0 else -1
+    if spec.accept is not None:
+        acc = np.asarray(spec.accept, np.int32)
+    else:
+        acc = rng.integers(0, spec.T + 1, size=B).astype(np.int32)
+        n0 = int(round(spec.zero_frac * B))
+        if n0:
+            acc[rng.permutation(B)[:n0]] = 0
+    tidx = tstep = None
+    if spec.track:
+        tidx = perm[B:2 * B].astype(np.int32)
+        tstep = rng.integers(-1, spec.T, size=B).astype(np.int32)
+    return idx, acc, tidx, tstep
+
+
+def _bf16_codes(vals: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(vals, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def make_gdn_problem(spec: GdnSpec, seed: int) -> GdnProblem:
+    """Host problem, every pool fully drawn: state N(0,1); raw k, v N(0,1)
+    in bf16; g ~ U(-1, 0) (decay exp(g) in (0.37, 1]); beta = sigmoid(N(0,1))."""
+    rng = np.random.default_rng(seed)
+    idx, acc, tidx, tstep = make_gdn_meta(spec, rng)
+    L, S, HV, H, T = spec.L, spec.slots, spec.HV, spec.H, spec.T
+    state = rng.standard_normal((L, S, HV, spec.dv, spec.dk), dtype=np.float32)
+    rawv = _bf16_codes(rng.standard_normal((L, S, HV, T, spec.dv), dtype=np.float32))
+    rawk = _bf16_codes(rng.standard_normal((L, S, H, T, spec.dk), dtype=np.float32))
+    g = rng.uniform(-1.0, 0.0, size=(L, S, HV, T)).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((L, S, HV, T))))).astype(np.float32)
+    return GdnProblem(spec, state, rawv, rawk, g, beta, idx, acc, tidx, tstep)
+
+
+@dataclasses.dataclass
+class GdnDeviceProblem:
+    spec: GdnSpec
+    state: object      # torch fp32 (L, slots, HV, dv, dk)
+    rawv: object       # torch bf16 (L, slots, HV, T, dv)
+    rawk: object       # torch bf16 (L, slots, H, T, dk)
+    g: object
+    beta: object
+    state_indices: np.ndarray
+    accept_lens: np.ndarray
+    track_state_indices: Optional[np.ndarray]
+    track_steps: Optional[np.ndarray]
+
+
+def make_gdn_device_problem(spec: GdnSpec, seed: int, device="cuda", fill: int = 0xA5) -> GdnDeviceProblem:
+    """Full-size device problem from a seeded torch generator: the live and
+    track slots' state, and every window, are drawn as in make_gdn_problem;
+    every other state byte holds `fill`."""
+    import torch
+    rng = np.random.default_rng(seed)
+    idx, acc, tidx, tstep = make_gdn_meta(spec, rng)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    L, S, HV, H, T = spec.L, spec.slots, spec.HV, spec.H, spec.T
+    state = torch.empty((L, S, HV, spec.dv, spec.dk), dtype=torch.float32, device=device)
+    state.view(torch.uint8).fill_(fill)
+    live = sorted(set(int(v) for v in idx if v > spec.null_block_id))
+    if live:
+        sl = torch.tensor(live, device=device)
+        for l in range(L):
+            state[l, sl] = torch.randn((len(live), HV, spec.dv, spec.dk), generator=gen, device=device)
+    rawv = torch.randn((L, S, HV, T, spec.dv), generator=gen, device=device).to(torch.bfloat16)
+    rawk = torch.randn((L, S, H, T, spec.dk), generator=gen, device=device).to(torch.bfloat16)
+    g = torch.rand((L, S, HV, T), generator=gen, device=device) - 1.0
+    beta = torch.sigmoid(torch.randn((L, S, HV, T), generator=gen, device=device))
+    return GdnDeviceProblem(spec, state, rawv, rawk, g, beta, idx, acc, tidx, tstep)
