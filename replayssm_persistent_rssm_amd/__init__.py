@@ -9,4 +9,5 @@ from ._binding import (  # noqa: F401
     RSSM_ERR_INVALID_ARGUMENT, RSSM_ERR_UNSUPPORTED, RSSM_OK, MaterializeCall, RssmDesc, RssmError, RssmTables,
     checkpoint_prefix_len, dtype_code, lib, make_desc, pointer_table, replayssm_materialize,
     rssm_debug_encode_rows, rssm_last_error, rssm_materialize, rssm_materialize_checkpoints,
-    rssm_materialize_launch_config, RSSM_MAX_CHECKPOINTS, stride_table)
+    rssm_materialize_launch_config, RSSM_MAX_CHECKPOINTS, stride_table, rssm_gdn_commit,
+    gated_delta_rule_replayssm_commit, GdnCommitCall, RssmGdnDesc, RssmGdnTables)

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "librssm_materialize.so")
 RSSM_F32, RSSM_BF16, RSSM_F16, RSSM_I8, RSSM_F8E4M3 = 0, 1, 2, 3, 4
 RSSM_OK, RSSM_ERR_INVALID_ARGUMENT, RSSM_ERR_UNSUPPORTED, RSSM_ERR_HIP = 0, 1, 2, 3
 EXPORTS = ("rssm_materialize", "rssm_materialize_checkpoints", "rssm_last_error", "rssm_materialize_launch_config",
-           "rssm_debug_encode_rows")
+           "rssm_debug_encode_rows", "rssm_gdn_commit")
 RSSM_MAX_CHECKPOINTS = 4
 _INT32_MAX = 2**31 - 1
 
@@ -49,6 +49,18 @@ class RssmTables(ctypes.Structure):
         "ring_start", "replay_prefix_len", "active_request_indices", "rand_seed")]
 
 
+class RssmGdnDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_layers", "slots", "num_v_heads", "num_k_heads", "window", "batch", "use_l2norm", "null_block_id",
+        "max_workgroups")]
+
+
+class RssmGdnTables(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "checkpoint_state", "rawv_cache", "rawk_cache", "g_cache", "beta_cache", "state_indices", "accept_lens",
+        "track_state_indices", "track_steps")]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -60,6 +72,8 @@ def _load():
     lib.rssm_materialize_checkpoints.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(RssmTables),
                                                  ctypes.c_int32, ctypes.c_void_p]
     lib.rssm_materialize_checkpoints.restype = ctypes.c_int
+    lib.rssm_gdn_commit.argtypes = [ctypes.POINTER(RssmGdnDesc), ctypes.POINTER(RssmGdnTables), ctypes.c_void_p]
+    lib.rssm_gdn_commit.restype = ctypes.c_int
     lib.rssm_last_error.argtypes = []
     lib.rssm_last_error.restype = ctypes.c_char_p
     lib.rssm_materialize_launch_config.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(ctypes.c_int32),
@@ -270,6 +284,69 @@ class MaterializeCall:
             self._tab.active_request_indices = _ptr(active_request_indices, "active_request_indices",
                                                     torch.int32, (self._batch,))
         st = self._call()
+        if st != RSSM_OK:
+            raise RssmError(st, rssm_last_error())
+
+
+def _gdn_marshal(checkpoint_state, rawv_cache, rawk_cache, g_cache, beta_cache, state_indices, accept_lens, *,
+                 track_state_indices=None, track_steps=None, use_qk_l2norm: bool = True, null_block_id: int = -1,
+                 max_workgroups: int = 0):
+    import torch
+    if checkpoint_state.dim() != 5 or tuple(checkpoint_state.shape[3:]) != (128, 128):
+        raise ValueError("checkpoint_state must be [layers, slots, HV, 128, 128]")
+    L, S, HV = (int(v) for v in checkpoint_state.shape[:3])
+    if rawv_cache.dim() != 5 or rawk_cache.dim() != 5:
+        raise ValueError("rawv_cache and rawk_cache must be 5-D [layers, slots, heads, T, 128]")
+    T = int(rawv_cache.shape[3])
+    H = int(rawk_cache.shape[2])
+    B = int(state_indices.shape[0])
+    if (track_state_indices is None) != (track_steps is None):
+        raise ValueError("track_state_indices and track_steps go together")
+    f32, bf16, i32 = torch.float32, torch.bfloat16, torch.int32
+    desc = RssmGdnDesc(num_layers=_scalar("num_layers", L), slots=_scalar("slots", S), num_v_heads=_scalar("HV", HV),
+                       num_k_heads=_scalar("H", H), window=_scalar("T", T), batch=_scalar("batch", B),
+                       use_l2norm=1 if use_qk_l2norm else 0, null_block_id=_scalar("null_block_id", null_block_id),
+                       max_workgroups=_scalar("max_workgroups", max_workgroups))
+    tab = RssmGdnTables(
+        checkpoint_state=_ptr(checkpoint_state, "checkpoint_state", f32, (L, S, HV, 128, 128)),
+        rawv_cache=_ptr(rawv_cache, "rawv_cache", bf16, (L, S, HV, T, 128)),
+        rawk_cache=_ptr(rawk_cache, "rawk_cache", bf16, (L, S, H, T, 128)),
+        g_cache=_ptr(g_cache, "g_cache", f32, (L, S, HV, T)),
+        beta_cache=_ptr(beta_cache, "beta_cache", f32, (L, S, HV, T)),
+        state_indices=_ptr(state_indices, "state_indices", i32, (B,)),
+        accept_lens=_ptr(accept_lens, "accept_lens", i32, (B,)),
+        track_state_indices=_ptr(track_state_indices, "track_state_indices", i32, (B,)),
+        track_steps=_ptr(track_steps, "track_steps", i32, (B,)))
+    return desc, tab
+
+
+def rssm_gdn_commit(*args, stream=None, **kw) -> None:
+    """Enqueue one gated-delta-rule commit (the page's
+    gated_delta_rule_replayssm_commit): checkpoint_state fp32 [L, slots, HV,
+    128, 128] updated in place; rawv_cache bf16 [L, slots, HV, T, 128];
+    rawk_cache bf16 [L, slots, H, T, 128]; g_cache and beta_cache fp32 [L,
+    slots, HV, T]; state_indices and accept_lens int32 [B].  Keywords:
+    track_state_indices / track_steps (int32 [B], both or neither),
+    use_qk_l2norm=True, null_block_id=-1, max_workgroups=0."""
+    desc, tab = _gdn_marshal(*args, **kw)
+    _check(_lib.rssm_gdn_commit(ctypes.byref(desc), ctypes.byref(tab), _stream_handle(stream)))
+
+
+# The page's name for the same call.
+gated_delta_rule_replayssm_commit = rssm_gdn_commit
+
+
+class GdnCommitCall:
+    """A prepared rssm_gdn_commit: arguments checked and marshalled once; each
+    call is one C call.  stream=None binds torch's current stream."""
+
+    def __init__(self, *args, stream=None, **kw):
+        self._desc, self._tab = _gdn_marshal(*args, **kw)
+        self._refs = (ctypes.byref(self._desc), ctypes.byref(self._tab))
+        self._stream = _stream_handle(stream)
+
+    def __call__(self) -> None:
+        st = _lib.rssm_gdn_commit(self._refs[0], self._refs[1], self._stream)
         if st != RSSM_OK:
             raise RssmError(st, rssm_last_error())
 

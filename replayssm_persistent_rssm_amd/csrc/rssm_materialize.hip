@@ -20,6 +20,8 @@
 #include <mutex>
 #include <unordered_map>
 
+#include "gdn_kernel.h"
+#include "rssm_gdn_commit.h"
 #include "rssm_kernel.h"
 #include "rssm_materialize.h"
 
@@ -34,6 +36,7 @@ const EncodeEntry* encoders_bf16(int* n);
 const EncodeEntry* encoders_f16(int* n);
 const EncodeEntry* encoders_i8(int* n);
 const EncodeEntry* encoders_f8(int* n);
+const void* gdn_kernel_for(int window);
 }  // namespace rssm
 
 namespace {
@@ -370,6 +373,77 @@ rssm_status rssm_materialize_checkpoints(const rssm_materialize_desc* desc, cons
     return fail(RSSM_ERR_INVALID_ARGUMENT, "num_checkpoints must be in [1, %d] (got %d)", RSSM_MAX_CHECKPOINTS,
                 num_checkpoints);
   return launch(desc, tables, num_checkpoints, hip_stream);
+}
+
+rssm_status rssm_gdn_commit(const rssm_gdn_commit_desc* d, const rssm_gdn_commit_tables* t, void* hip_stream) {
+  g_err[0] = '\0';
+  if (d == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->num_layers < 1) return fail(RSSM_ERR_INVALID_ARGUMENT, "num_layers must be >= 1 (got %d)", d->num_layers);
+  if (d->slots < 1) return fail(RSSM_ERR_INVALID_ARGUMENT, "slots must be >= 1 (got %d)", d->slots);
+  if (d->num_v_heads < 1 || d->num_k_heads < 1 || d->num_v_heads % d->num_k_heads != 0)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "num_k_heads (%d) must be >= 1 and divide num_v_heads (%d)",
+                d->num_k_heads, d->num_v_heads);
+  if (d->window < 1 || d->window > 16)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "window must be in [1, 16] (got %d)", d->window);
+  if (d->batch < 0) return fail(RSSM_ERR_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", d->batch);
+  if (d->use_l2norm != 0 && d->use_l2norm != 1)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "use_l2norm must be 0 or 1 (got %d)", d->use_l2norm);
+  if (d->null_block_id < -1)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "null_block_id must be >= -1 (got %d)", d->null_block_id);
+  if (d->max_workgroups < 0)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "max_workgroups must be >= 0 (got %d)", d->max_workgroups);
+  const int64_t tiles = static_cast<int64_t>(d->num_layers) * d->slots * d->num_v_heads;
+  if (tiles > (int64_t(1) << 40))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "num_layers*slots*num_v_heads = %lld exceeds 2^40",
+                static_cast<long long>(tiles));
+  if (static_cast<int64_t>(d->batch) * d->num_layers * d->num_v_heads > (int64_t(1) << 40))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "batch*num_layers*num_v_heads exceeds 2^40");
+  if (t == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "tables is NULL");
+  struct P { const void* p; const char* n; int align; };
+  const P ptrs[] = {{t->checkpoint_state, "checkpoint_state", 16}, {t->rawv_cache, "rawv_cache", 16},
+                    {t->rawk_cache, "rawk_cache", 16}, {t->g_cache, "g_cache", 4}, {t->beta_cache, "beta_cache", 4},
+                    {t->state_indices, "state_indices", 4}, {t->accept_lens, "accept_lens", 4}};
+  for (const P& e : ptrs) {
+    if (e.p == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is NULL", e.n);
+    if (!aligned(e.p, e.align)) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", e.n, e.align);
+  }
+  if ((t->track_state_indices == nullptr) != (t->track_steps == nullptr))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "track_state_indices and track_steps go together (both or neither)");
+  if (t->track_state_indices != nullptr && (!aligned(t->track_state_indices, 4) || !aligned(t->track_steps, 4)))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "track tables are not 4-byte aligned");
+  if (d->batch == 0) return RSSM_OK;
+  const void* fn = rssm::gdn_kernel_for(d->window);
+  int grid = d->max_workgroups;
+  if (grid == 0) {
+    rssm_status st = grid_for(fn, &grid);
+    if (st != RSSM_OK) return st;
+  }
+  rssm::GdnArgs args;
+  args.state = t->checkpoint_state;
+  args.rawv = t->rawv_cache;
+  args.rawk = t->rawk_cache;
+  args.g = t->g_cache;
+  args.beta = t->beta_cache;
+  args.state_indices = t->state_indices;
+  args.accept_lens = t->accept_lens;
+  args.track_indices = t->track_state_indices;
+  args.track_steps = t->track_steps;
+  args.L = d->num_layers;
+  args.slots = d->slots;
+  args.HV = d->num_v_heads;
+  args.H = d->num_k_heads;
+  args.T = d->window;
+  args.B = d->batch;
+  args.use_l2norm = d->use_l2norm;
+  args.null_block_id = d->null_block_id;
+  if (verbose())
+    std::fprintf(stderr, "[rssm_gdn_commit] window<=%d grid=%d block=%d L=%d B=%d HV=%d H=%d\n",
+                 d->window <= 8 ? 8 : 16, grid, rssm::kBlock, d->num_layers, d->batch, d->num_v_heads,
+                 d->num_k_heads);
+  void* params[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(rssm::kBlock), params, 0, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(RSSM_ERR_HIP, "launch of gdn_commit failed: %s", hipGetErrorString(e));
+  return RSSM_OK;
 }
 
 rssm_status rssm_debug_encode_rows(const rssm_materialize_desc* desc, const float* rows, const int32_t* coords,

@@ -193,3 +193,21 @@ def flush_and_checkpoint_tables(meta: ri.Meta):
     dst = np.stack([meta.src, meta.dst]).astype(np.int32)
     pre = np.stack([meta.prefix, meta.prefix // 2]).astype(np.int32)
     return dst, pre
+
+
+def gdn_bytes(spec: ri.GdnSpec, idx, acc, tidx=None, tstep=None) -> int:
+    """Bytes a gated-delta-rule commit must move: per committed (request,
+    layer, value head) the fp32 state read and written (+ written once more for
+    a tracked step inside the prefix) and the n accepted tokens' value rows, g
+    and beta; per (request, layer, key head) the n key rows."""
+    tile = spec.dv * spec.dk * 4
+    total = 0
+    for b in range(spec.B):
+        n = int(acc[b])
+        if int(idx[b]) <= spec.null_block_id or n <= 0:
+            continue
+        n = min(n, spec.T)
+        tracked = tidx is not None and int(tidx[b]) > spec.null_block_id and 0 <= int(tstep[b]) < n
+        per_head = 2 * tile + (tile if tracked else 0) + n * (spec.dv * 2 + 8)
+        total += spec.L * (spec.HV * per_head + spec.H * n * spec.dk * 2)
+    return total

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rssm_materialize.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -19,9 +20,11 @@ def rp():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rssm_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(rssm_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_entry_point(rp):
@@ -169,3 +172,51 @@ def test_checkpoint_byte_count(rp):
     ring = spec.H * spec.dim * 2 + spec.G * spec.dstate * 2 + spec.H * 4
     want = sum(spec.L * (3 * tile + int(meta.prefix[b]) * ring) for b in range(spec.B)) + spec.L * spec.H * 4
     assert hx.checkpoint_bytes(spec, meta, dst, pre) == want
+
+
+def _gdn_desc(rp, **kw):
+    base = dict(num_layers=48, slots=512, num_v_heads=32, num_k_heads=16, window=8, batch=256, use_l2norm=1,
+                null_block_id=-1, max_workgroups=0)
+    base.update(kw)
+    return rp.RssmGdnDesc(**base)
+
+
+def _gdn_tables(rp, **override):
+    t = rp.RssmGdnTables(**{f: 0x10000 for f, _ in rp.RssmGdnTables._fields_})
+    for k, v in override.items():
+        setattr(t, k, v)
+    return t
+
+
+BAD_GDN = [
+    (dict(num_layers=0), "num_layers"), (dict(slots=0), "slots"), (dict(num_k_heads=3), "divide"),
+    (dict(num_v_heads=0), "divide"), (dict(window=0), "window"), (dict(window=17), "window"),
+    (dict(batch=-1), "batch"), (dict(use_l2norm=2), "use_l2norm"), (dict(null_block_id=-2), "null_block_id"),
+    (dict(max_workgroups=-1), "max_workgroups"), (dict(num_layers=2**20, slots=2**20, num_v_heads=2, num_k_heads=1), "2^40"),
+]
+
+
+@pytest.mark.parametrize("kw,text", BAD_GDN)
+def test_gdn_bad_scalars_rejected(rp, kw, text):
+    d = _gdn_desc(rp, **kw)
+    t = _gdn_tables(rp)
+    assert rp.lib().rssm_gdn_commit(ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert text in rp.rssm_last_error()
+
+
+def test_gdn_tables_rejected(rp):
+    d = _gdn_desc(rp)
+    assert rp.lib().rssm_gdn_commit(ctypes.byref(d), None, None) == 1
+    assert rp.lib().rssm_gdn_commit(None, None, None) == 1
+    for field in ("checkpoint_state", "rawk_cache", "beta_cache", "accept_lens"):
+        t = _gdn_tables(rp, **{field: None})
+        assert rp.lib().rssm_gdn_commit(ctypes.byref(d), ctypes.byref(t), None) == 1
+        assert field in rp.rssm_last_error()
+    t = _gdn_tables(rp, rawv_cache=0x10008)
+    assert rp.lib().rssm_gdn_commit(ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert "aligned" in rp.rssm_last_error()
+    t = _gdn_tables(rp, track_steps=None)
+    assert rp.lib().rssm_gdn_commit(ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert "track" in rp.rssm_last_error()
+    # an empty batch enqueues nothing and touches no device
+    assert rp.lib().rssm_gdn_commit(ctypes.byref(_gdn_desc(rp, batch=0)), ctypes.byref(_gdn_tables(rp)), None) == 0
