@@ -127,6 +127,8 @@ def main():
                     help="counter mode: 2 full-batch calls, then 2 plain device copies of 1 GiB")
     ap.add_argument("--workload", default=WORKLOAD, choices=["large_bf16", "large_i8", "large_f8sr"],
                     help="workload of the profile modes (the headline line always uses large_bf16)")
+    ap.add_argument("--only-gdn", action="store_true",
+                    help="profile mode: the gated-delta-rule commit line only")
     ap.add_argument("--only-checkpoints", action="store_true",
                     help="profile mode: the multi-checkpoint line of the large_bf16 workload only")
     ap.add_argument("--no-checkpoints", action="store_true",
@@ -160,6 +162,9 @@ def main():
     import replayssm_persistent_rssm_amd as rp
 
     dev = torch.device("cuda:0")
+    if args.only_gdn:
+        print(json.dumps({"gdn_commit": gdn_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
+        return
     profile_mode = args.only_main or args.empty_only or args.pmc_calibrate or args.only_checkpoints
     wl = args.workload if profile_mode else WORKLOAD
     spec = ri.CONFIGS[wl]
@@ -326,6 +331,7 @@ def main():
         torch.cuda.empty_cache()
         result["other_workloads"] = {name: other_workload(name, dev, stream, max(5, args.steps // 2))
                                      for name in ("large_i8", "large_f8sr")}
+        result["other_workloads"]["gdn_commit"] = gdn_workload(dev, stream, max(5, args.steps // 2))
     print(json.dumps(result), flush=True)
 
 
@@ -366,6 +372,43 @@ def checkpoint_workload(dp, tabs, spec, stream, steps):
            "two_single_calls_ms": round(ms_two, 4),
            "speedup_vs_two_calls": round(ms_two / ms_multi, 3)}
     say(f"checkpoints: {out}")
+    return out
+
+
+def gdn_workload(dev, stream, steps):
+    """The gated-delta-rule commit on gdn_large: 48 layers, 256 requests (a
+    sixteenth with a null slot, a sixteenth accepting nothing, the rest
+    accepting U[0, 8] tokens), 32 value heads over 16 key heads, fp32 128x128
+    checkpoints, 8-token bf16 windows, a tracked step per request (inside the
+    prefix for about half).  The commit is in place, so timed calls keep
+    evolving the states (the update never expands them)."""
+    import torch
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    import replayssm_persistent_rssm_amd as rp
+    spec = ri.GDN_CONFIGS["gdn_large"]
+    seed = 1010
+    say("generating gdn_large seed", seed)
+    dp = ri.make_gdn_device_problem(spec, seed, dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+    meta = [i32(dp.state_indices), i32(dp.accept_lens), i32(dp.track_state_indices), i32(dp.track_steps)]
+    call = rp.GdnCommitCall(dp.state, dp.rawv, dp.rawk, dp.g, dp.beta, meta[0], meta[1],
+                            track_state_indices=meta[2], track_steps=meta[3], null_block_id=spec.null_block_id)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ms = timed_calls(call, steps, stream)
+    nbytes = hx.gdn_bytes(spec, dp.state_indices, dp.accept_lens, dp.track_state_indices, dp.track_steps)
+    live = int(sum(1 for b in range(spec.B) if dp.state_indices[b] > spec.null_block_id and dp.accept_lens[b] > 0))
+    out = {"workload": f"gdn_large: L={spec.L}, B={spec.B} ({live} committing), HV={spec.HV}, H={spec.H}, "
+                       f"fp32 128x128 K-last state, bf16 windows T={spec.T}, tracked steps",
+           "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+           "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "us_per_request": round(ms * 1e3 / max(live, 1), 3)}
+    say(f"gdn_commit: {out}")
+    del call, dp, meta
+    torch.cuda.empty_cache()
     return out
 
 
@@ -462,16 +505,16 @@ def counters_summary(fetch_csv, write_csv):
 
 
 def pmc_summary(path):
-    """One line per materialize dispatch: dispatch id, then counter=value."""
+    """One line per dispatch of a library kernel: dispatch id, kernel, then counter=value."""
     import csv
     rows = {}
     with open(path) as f:
         for r in csv.DictReader(f):
-            if "materialize_kernel" not in r["Kernel_Name"]:
+            if "rssm::" not in r["Kernel_Name"]:
                 continue
-            d = rows.setdefault(int(r["Dispatch_Id"]), {})
+            d = rows.setdefault(int(r["Dispatch_Id"]), {"": r["Kernel_Name"].split("(")[0].replace("void ", "")})
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    return "".join(f"dispatch {d}: " + " ".join(f"{k}={v:.6g}" for k, v in sorted(c.items())) + "\n"
+    return "".join(f"dispatch {d} {c.pop('')}: " + " ".join(f"{k}={v:.6g}" for k, v in sorted(c.items())) + "\n"
                    for d, c in sorted(rows.items()))
 
 

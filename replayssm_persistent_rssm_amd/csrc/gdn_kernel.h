@@ -13,25 +13,23 @@
 // track_steps[b] also goes to slot track_state_indices[b].
 //
 // Design (MI355X, wave64):
-//  * Work item = an eighth of a tile: 16 value rows x 128 key columns (8 KiB
-//    contiguous) of one (request, layer, value head).  Each wavefront owns a
-//    contiguous range of items (request-major, then layer, head, quarter), so
-//    consecutive items share the request's metadata and often its keys.  No
-//    workgroup barriers.
-//  * 16 lanes per row, 8 columns per lane: a lane holds 4 rows x 8 columns
-//    of S (32 registers) for the whole token loop (32 rows per item needed
-//    about 200 registers and halved the resident waves); S is read once and written
-//    once per commit (plus once more for a tracked step).
-//  * Keys are normalised once per (request, layer, key head) into the
-//    wavefront's LDS ([token][column], fp32); the item's 16 values per token go
-//    to LDS as [token][row-in-pass][pass], so a lane reads its 4 rows with one
-//    16-byte load.
-//  * Per token and row, S k is 8 fused multiply-adds per lane and a 16-lane
+//  * The update never mixes rows of S: row i evolves by its own dot product
+//    with the token's key.  So a state tile is streamed row-wise, like the
+//    materialize kernel's: 16 lanes per row, 8 key columns per lane, 4 rows
+//    per wavefront pass, PD passes in flight while earlier passes run their
+//    tokens.  Work item = one (request, layer, value head) tile; tiles are
+//    dealt round-robin over the wavefronts, so each sees the same mix of
+//    cheap (skipped), plain and tracked requests.  No workgroup barriers.
+//  * The normalised keys live in registers (8 columns x up to TMAX tokens per
+//    lane, normalised with a 16-lane DPP sum of squares); the tile's values go
+//    to the wavefront's LDS as [row][token]; decays and betas sit one token
+//    per lane and are read with readlane.
+//  * Per token and row: S k is 8 fused multiply-adds per lane and a 16-lane
 //    DPP sum; the update S <- exp(g) S + u k^T with u = beta (v - exp(g) S k)
-//    is 2 VALU operations per element.  fp32 throughout (the contractions are
+//    is 2 VALU operations per element.  fp32 throughout: the contractions are
 //    matrix-vector products with a sequential dependence between tokens, and
-//    the path is bound by HBM: 128 KiB of state per (request, layer, head)
-//    against ~3 VALU operations per element per token).
+//    the path moves 128 KiB of state per tile against ~4 VALU operations per
+//    element per token, so HBM bounds it.
 #pragma once
 
 #include "rssm_kernel.h"
@@ -52,7 +50,6 @@ struct GdnArgs {
 };
 
 constexpr int kGdnDim = 128;   // key and value width, fixed by the page
-constexpr int kGdnRows = 16;   // value rows per work item (an eighth of a tile)
 
 // Sum over the 16 lanes of an aligned lane group (the same exchange pattern
 // as row16_max).
@@ -64,163 +61,187 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-template <int TMAX>
-__global__ void __launch_bounds__(kBlock, 4) gdn_commit_kernel(const GdnArgs a) {
+// Register budget: the keys cost 8 * TMAX registers per lane.
+template <int TMAX> constexpr int kGdnWavesPerSimd = (TMAX > 8) ? 2 : 3;
+
+// Stream knobs (the library's instances use the defaults; the others exist so
+// that streaming patterns can be compared on hardware).  Measured on MI355X,
+// variants side by side in one process (48 layers, 256 requests, 32 value
+// heads): with 4 tokens each, cached state loads and stores with 2 passes in
+// flight ran 9.45 ms, non-temporal ones 10.5 ms, 4 passes in flight 10.2 ms;
+// with the benchmark's mix (prefixes U[0, 8], a sixteenth null, tracked steps)
+// dealing tiles round-robin ran 10.2 ms against 13.0 ms for contiguous ranges,
+// and a 3-wave register budget 9.8 ms.
+//   NTL / NTS  non-temporal state loads / stores
+//   PD         state passes in flight per wavefront
+//   WPS        waves per SIMD the registers are budgeted for (0: the rule above)
+//   DEAL       work distribution (below)
+template <int TMAX, bool NTL = false, bool NTS = false, int PD = 2, int WPS = 0, int DEAL = 1>
+__global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX>))
+    gdn_commit_kernel(const GdnArgs a) {
   constexpr int D = kGdnDim;
   constexpr int TPR = 16;                 // lanes per row
   constexpr int RPP = 64 / TPR;           // rows per pass (4)
-  constexpr int NP = kGdnRows / RPP;      // passes per item (4)
+  constexpr int NPASS = D / RPP;          // passes per tile (32)
   constexpr int64_t kTile = static_cast<int64_t>(D) * D;
-  constexpr int QPT = D / kGdnRows;       // items per tile (8)
-  static_assert(TMAX >= 1 && TMAX <= 16, "TMAX");
-  static_assert(NP % 4 == 0 && D % kGdnRows == 0, "item shape");
+  constexpr int PS = RPP * D * 4;         // bytes between passes
+  static_assert(TMAX % 4 == 0 && TMAX <= 16, "TMAX");
+  static_assert(NPASS % PD == 0, "passes must split into prefetch groups");
 
-  __shared__ __attribute__((aligned(16))) float lds_k[kWaves][TMAX * D];
-  __shared__ __attribute__((aligned(16))) float lds_v[kWaves][TMAX * kGdnRows];
+  __shared__ __attribute__((aligned(16))) float lds_v[kWaves][D * TMAX];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
-  float* kw = lds_k[wave];
   float* vw = lds_v[wave];
   const int cc = lane % TPR;
   const int rr = lane / TPR;
   const uint32_t lane_off = static_cast<uint32_t>((rr * D + cc * 8) * 4);  // bytes, in a pass
-  constexpr int PS = RPP * D * 4;                                            // bytes between passes
 
-  const int64_t per_req = static_cast<int64_t>(a.L) * a.HV * QPT;
+  const int64_t per_req = static_cast<int64_t>(a.L) * a.HV;
   const int64_t items = static_cast<int64_t>(a.B) * per_req;
   const int64_t tw = static_cast<int64_t>(gridDim.x) * kWaves;
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  const int64_t per = items / tw, rem = items % tw;
-  int64_t it = gw * per + (gw < rem ? gw : rem);
-  const int64_t end = it + per + (gw < rem ? 1 : 0);
+  // DEAL = 0: one contiguous, balanced range of tiles per wavefront.
+  // DEAL = 1: tiles dealt round-robin (wavefront w takes w, w + waves, ...),
+  // so that every wavefront sees the same mix of requests -- their costs
+  // differ (skipped, tracked, short or long prefixes).
+  int64_t it, end;
+  if constexpr (DEAL == 0) {
+    const int64_t per = items / tw, rem = items % tw;
+    it = gw * per + (gw < rem ? gw : rem);
+    end = it + per + (gw < rem ? 1 : 0);
+  } else {
+    it = gw;
+    end = items;
+  }
+  constexpr int64_t kOne = 1;
+  const int64_t advance = DEAL ? tw : kOne;
   const int group = a.HV / a.H;
-  int64_t staged_key = -1;  // (request, layer, key head) whose keys are in LDS
+
+  int cur_b = -1, s = 0, n = 0, ts = -1, step = -1;
+  bool live = false;
 
   while (it < end) {
     const int b = static_cast<int>(it / per_req);
-    const int64_t in_req = it - static_cast<int64_t>(b) * per_req;
-    const int s = uniform(a.state_indices[b]);
-    int n = uniform(a.accept_lens[b]);
-    if (s <= a.null_block_id || s >= a.slots || n <= 0) {
-      it = min(end, static_cast<int64_t>(b + 1) * per_req);   // ignored slot or nothing accepted
+    if (b != cur_b) {
+      // Request metadata, read when the request changes.
+      cur_b = b;
+      s = uniform(a.state_indices[b]);
+      n = uniform(a.accept_lens[b]);
+      live = s > a.null_block_id && s < a.slots && n > 0;   // else ignored slot or nothing accepted
+      n = min(n, a.T);
+      step = -1;
+      if (live && a.track_indices != nullptr) {
+        ts = uniform(a.track_indices[b]);
+        step = uniform(a.track_steps[b]);
+        if (ts <= a.null_block_id || ts >= a.slots || step < 0 || step >= n) step = -1;  // not written
+      }
+    }
+    if (!live) {
+      if constexpr (DEAL == 0) it = min(end, static_cast<int64_t>(b + 1) * per_req);
+      else it += advance;
       continue;
     }
-    n = min(n, a.T);
-    int ts = -1, step = -1;
-    if (a.track_indices != nullptr) {
-      ts = uniform(a.track_indices[b]);
-      step = uniform(a.track_steps[b]);
-      if (ts <= a.null_block_id || ts >= a.slots || step < 0 || step >= n) step = -1;  // not written
-    }
-    const int l = static_cast<int>(in_req / (static_cast<int64_t>(a.HV) * QPT));
-    const int hq = static_cast<int>(in_req - static_cast<int64_t>(l) * a.HV * QPT);
-    const int hv = hq / QPT;
-    const int q = hq - hv * QPT;
+    const int64_t in_req = it - static_cast<int64_t>(b) * per_req;
+    const int l = static_cast<int>(in_req / a.HV);
+    const int hv = static_cast<int>(in_req - static_cast<int64_t>(l) * a.HV);
     const int kh = hv / group;
+    it += advance;
     const int64_t vslot = (static_cast<int64_t>(l) * a.slots + s) * a.HV + hv;   // (l, s, hv)
-    char* tile = reinterpret_cast<char*>(a.state + vslot * kTile + static_cast<int64_t>(q) * kGdnRows * D);
+    const char* tile = reinterpret_cast<const char*>(a.state + vslot * kTile);
+    char* otile = reinterpret_cast<char*>(a.state + vslot * kTile);
+    char* ttile = step >= 0 ? reinterpret_cast<char*>(a.state + ((static_cast<int64_t>(l) * a.slots + ts) * a.HV + hv) * kTile)
+                            : nullptr;
 
-    // Issue the item's 16 x 128 fp32 block: 4 passes x 32 bytes per lane.
-    Chunk<kF32> S[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) S[p] = load_chunk<kF32, true>(at(tile + p * PS, lane_off));
-
-    // Keys of (b, l, kh), normalised, unless already staged.
-    const int64_t key_id = (static_cast<int64_t>(b) * a.L + l) * a.H + kh;
-    wave_lds_fence();
-    if (key_id != staged_key) {
-      const uint16_t* kwin = a.rawk + ((static_cast<int64_t>(l) * a.slots + s) * a.H + kh) * a.T * D;
-#pragma unroll
-      for (int rep = 0; rep < (TMAX * TPR + 63) / 64; ++rep) {
-        const int t = rep * RPP + rr;        // 16 lanes per token
-        float kv[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        if (t < n) {
-          const Chunk<kBF16> c = load_chunk<kBF16>(reinterpret_cast<const char*>(kwin + t * D + cc * 8));
-          decode_chunk<kBF16>(c, kv);
-        }
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss = fmaf(kv[i], kv[i], ss);
-        ss = row16_sum(ss);
-        const float inv = a.use_l2norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
-        if (t < n) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kw[t * D + cc * 8 + i] = kv[i] * inv;
-        }
-      }
-      staged_key = key_id;
+    // Small inputs first, the state stream after them (a wavefront's memory
+    // requests complete in order, so staging waits only for these).
+    float g_l = 0.0f, beta_l = 0.0f;       // token `lane`
+    if (lane < n) {
+      g_l = gload(a.g + vslot * a.T + lane);
+      beta_l = gload(a.beta + vslot * a.T + lane);
     }
-    // Values of this item's 16 rows: token t, row p*4 + rr -> vw[t*16 + rr*4 + p].
-    {
-      const uint16_t* vwin = a.rawv + vslot * a.T * D + q * kGdnRows;
-#pragma unroll
-      for (int rep = 0; rep < (TMAX * kGdnRows + 63) / 64; ++rep) {
-        const int idx = rep * 64 + lane;
-        const int t = idx / kGdnRows;
-        const int row = idx % kGdnRows;
-        if (t < n) {
-          const float v = __uint_as_float(static_cast<uint32_t>(gload(vwin + t * D + row)) << 16);
-          vw[t * kGdnRows + (row % RPP) * NP + row / RPP] = v;
-        }
-      }
-    }
-    wave_lds_fence();
-
-    const float* gw_ = a.g + vslot * a.T;
-    const float* bw_ = a.beta + vslot * a.T;
-    float Sf[NP][8];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) decode_chunk<kF32>(S[p], Sf[p]);
-
+    const uint16_t* vwin = a.rawv + vslot * a.T * D;
+    uint32_t vraw[TMAX][2];                // token t, rows lane and lane + 64
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
-      if (t >= n) break;
-      const float alpha = expf(gload(gw_ + t));
-      const float bt = gload(bw_ + t);
-      const float4 k0 = *reinterpret_cast<const float4*>(kw + t * D + cc * 8);
-      const float4 k1 = *reinterpret_cast<const float4*>(kw + t * D + cc * 8 + 4);
-      const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-      float vv[NP];
+      vraw[t][0] = (t < n) ? gload(vwin + t * D + lane) : 0u;
+      vraw[t][1] = (t < n) ? gload(vwin + t * D + 64 + lane) : 0u;
+    }
+    // The tile's keys (re-read per tile: the heads of one key head find them
+    // in L2), 16 lanes per token row.
+    Chunk<kBF16> kraw[TMAX];
+    const uint16_t* kwin = a.rawk + ((static_cast<int64_t>(l) * a.slots + s) * a.H + kh) * a.T * D;
 #pragma unroll
-      for (int i = 0; i < NP; i += 4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(vw + t * kGdnRows + rr * NP + i);
-        vv[i] = v4.x;
-        vv[i + 1] = v4.y;
-        vv[i + 2] = v4.z;
-        vv[i + 3] = v4.w;
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < n) kraw[t] = load_chunk<kBF16>(reinterpret_cast<const char*>(kwin + t * D + cc * 8));
+      else kraw[t] = Chunk<kBF16>{};
+    }
+    Chunk<kF32> buf[PD];
+#pragma unroll
+    for (int p = 0; p < PD; ++p) buf[p] = load_chunk<kF32, NTL>(at(tile + p * PS, lane_off));
+
+    const float alpha_l = expf(g_l);
+    float kv[TMAX][8];                     // normalised keys, this lane's 8 columns
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      decode_chunk<kBF16>(kraw[t], kv[t]);
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(kv[t][i], kv[t][i], ss);
+      ss = row16_sum(ss);
+      const float inv = a.use_l2norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kv[t][i] *= inv;
+    }
+    // Values to LDS as [row][token].
+    wave_lds_fence();
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < n) {
+        vw[lane * TMAX + t] = __uint_as_float(vraw[t][0] << 16);
+        vw[(lane + 64) * TMAX + t] = __uint_as_float(vraw[t][1] << 16);
       }
+    }
+    wave_lds_fence();
+
+    // Stream the tile: PD passes in flight; each pass runs the n tokens on
+    // its rows and is written back (and, after the tracked token, copied).
+#pragma unroll 1
+    for (int p0 = 0; p0 < NPASS; p0 += PD) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        float d = 0.0f;
+      for (int q = 0; q < PD; ++q) {
+        const int p = p0 + q;
+        const Chunk<kF32> cur = buf[q];
+        if (p + PD < NPASS) buf[q] = load_chunk<kF32, NTL>(at(tile + (p + PD) * PS, lane_off));
+        const int r = rr + p * RPP;
+        float S[8];
+        decode_chunk<kF32>(cur, S);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) d = fmaf(Sf[p][c], kv[c], d);
-        d = row16_sum(d);                           // (S k)[row], before the decay
-        const float u = bt * (vv[p] - alpha * d);   // beta (v - exp(g) S k)
+        for (int t = 0; t < TMAX; ++t) {
+          if (t < n) {
+            const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha_l), t));
+            const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(beta_l), t));
+            float d = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) Sf[p][c] = fmaf(Sf[p][c], alpha, u * kv[c]);
-      }
-      if (t == step) {
-        char* ttile = reinterpret_cast<char*>(
-            a.state + ((static_cast<int64_t>(l) * a.slots + ts) * a.HV + hv) * kTile +
-            static_cast<int64_t>(q) * kGdnRows * D);
+            for (int c = 0; c < 8; ++c) d = fmaf(S[c], kv[t][c], d);
+            d = row16_sum(d);                           // (S k)[row], before the decay
+            const float u = bt * (vw[r * TMAX + t] - alpha * d);   // beta (v - exp(g) S k)
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          Chunk<kF32> c;
+            for (int c = 0; c < 8; ++c) S[c] = fmaf(S[c], alpha, u * kv[t][c]);
+            if (t == step) {
+              Chunk<kF32> o;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) c.w[i] = __float_as_uint(Sf[p][i]);
-          store_chunk<kF32, true>(at(ttile + p * PS, lane_off), c);
+              for (int c = 0; c < 8; ++c) o.w[c] = __float_as_uint(S[c]);
+              store_chunk<kF32, NTS>(at(ttile + p * PS, lane_off), o);
+            }
+          }
         }
+        Chunk<kF32> o;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o.w[c] = __float_as_uint(S[c]);
+        store_chunk<kF32, NTS>(at(otile + p * PS, lane_off), o);
       }
     }
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      Chunk<kF32> c;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c.w[i] = __float_as_uint(Sf[p][i]);
-      store_chunk<kF32, true>(at(tile + p * PS, lane_off), c);
-    }
-    ++it;
   }
 }
 
