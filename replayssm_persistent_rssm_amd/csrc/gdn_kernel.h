@@ -76,7 +76,8 @@ template <int TMAX> constexpr int kGdnWavesPerSimd = (TMAX > 8) ? 2 : 3;
 //   PD         state passes in flight per wavefront
 //   WPS        waves per SIMD the registers are budgeted for (0: the rule above)
 //   DEAL       work distribution (below)
-template <int TMAX, bool NTL = false, bool NTS = false, int PD = 2, int WPS = 0, int DEAL = 1>
+//   KLDS       keys in the wavefront's LDS (read per token) instead of registers
+template <int TMAX, bool NTL = false, bool NTS = false, int PD = 2, int WPS = 0, int DEAL = 1, bool KLDS = false>
 __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX>))
     gdn_commit_kernel(const GdnArgs a) {
   constexpr int D = kGdnDim;
@@ -89,6 +90,7 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
   static_assert(NPASS % PD == 0, "passes must split into prefetch groups");
 
   __shared__ __attribute__((aligned(16))) float lds_v[kWaves][D * TMAX];
+  __shared__ __attribute__((aligned(16))) float lds_k[kWaves][KLDS ? TMAX * D : 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
@@ -181,20 +183,30 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
     for (int p = 0; p < PD; ++p) buf[p] = load_chunk<kF32, NTL>(at(tile + p * PS, lane_off));
 
     const float alpha_l = expf(g_l);
-    float kv[TMAX][8];                     // normalised keys, this lane's 8 columns
+    wave_lds_fence();
+    float kv[KLDS ? 1 : TMAX][8];          // normalised keys, this lane's 8 columns
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
-      decode_chunk<kBF16>(kraw[t], kv[t]);
+      float k8[8];
+      decode_chunk<kBF16>(kraw[t], k8);
       float ss = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(kv[t][i], kv[t][i], ss);
+      for (int i = 0; i < 8; ++i) ss = fmaf(k8[i], k8[i], ss);
       ss = row16_sum(ss);
       const float inv = a.use_l2norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kv[t][i] *= inv;
+      for (int i = 0; i < 8; ++i) k8[i] *= inv;
+      if constexpr (KLDS) {
+        if (rr == 0) {
+          *reinterpret_cast<float4*>(&lds_k[wave][t * D + cc * 8]) = make_float4(k8[0], k8[1], k8[2], k8[3]);
+          *reinterpret_cast<float4*>(&lds_k[wave][t * D + cc * 8 + 4]) = make_float4(k8[4], k8[5], k8[6], k8[7]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kv[t][i] = k8[i];
+      }
     }
     // Values to LDS as [row][token].
-    wave_lds_fence();
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < n) {
@@ -221,13 +233,23 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
           if (t < n) {
             const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha_l), t));
             const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(beta_l), t));
+            float kt[8];
+            if constexpr (KLDS) {
+              const float4 k0 = *reinterpret_cast<const float4*>(&lds_k[wave][t * D + cc * 8]);
+              const float4 k1 = *reinterpret_cast<const float4*>(&lds_k[wave][t * D + cc * 8 + 4]);
+              kt[0] = k0.x; kt[1] = k0.y; kt[2] = k0.z; kt[3] = k0.w;
+              kt[4] = k1.x; kt[5] = k1.y; kt[6] = k1.z; kt[7] = k1.w;
+            } else {
+#pragma unroll
+              for (int c = 0; c < 8; ++c) kt[c] = kv[KLDS ? 0 : t][c];
+            }
             float d = 0.0f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) d = fmaf(S[c], kv[t][c], d);
+            for (int c = 0; c < 8; ++c) d = fmaf(S[c], kt[c], d);
             d = row16_sum(d);                           // (S k)[row], before the decay
             const float u = bt * (vw[r * TMAX + t] - alpha * d);   // beta (v - exp(g) S k)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) S[c] = fmaf(S[c], alpha, u * kv[t][c]);
+            for (int c = 0; c < 8; ++c) S[c] = fmaf(S[c], alpha, u * kt[c]);
             if (t == step) {
               Chunk<kF32> o;
 #pragma unroll

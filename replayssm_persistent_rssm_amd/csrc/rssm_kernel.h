@@ -94,10 +94,13 @@ __device__ __forceinline__ int count_active(const int32_t* active, int B, int la
   return B;
 }
 
-// Value of lane-permuted v within each 16-lane DPP row (no LDS traffic).
+// Value of lane-permuted v within each 16-lane DPP row (no LDS traffic).  The
+// patterns used here have a valid source lane for every lane, so bound_ctrl
+// never applies; a plain DPP move (rather than an update of an old value)
+// lets the compiler fold it into the consuming add or max.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Max over the 16 lanes of an aligned lane group (one state row): swap lane
