@@ -79,17 +79,19 @@ __device__ __forceinline__ void wave_lds_fence() {
 // Number of requests before the first entry that is -1 (or outside [0, B)).
 __device__ __forceinline__ int count_active(const int32_t* active, int B, int lane) {
   for (int base = 0; base < B; base += 256) {
-    int v[4];
+    // All four loads are issued before any is used (indices past B read the
+    // last entry and are then discarded), so the scan costs one round trip.
+    uint64_t stop[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int idx = base + 64 * q + lane;
-      v[q] = (idx < B) ? active[idx] : -1;
+      const int x = gload(active + (idx < B ? idx : B - 1));
+      const int v = (idx < B) ? x : -1;
+      stop[q] = __ballot(v < 0 || v >= B);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint64_t stop = __ballot(v[q] < 0 || v[q] >= B);
-      if (stop) return base + 64 * q + __builtin_ctzll(stop);
-    }
+    for (int q = 0; q < 4; ++q)
+      if (stop[q]) return base + 64 * q + __builtin_ctzll(stop[q]);
   }
   return B;
 }
@@ -362,15 +364,37 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
 
     const int i = static_cast<int>(il / a.L);
     const int l = static_cast<int>(il - static_cast<int64_t>(i) * a.L);
-    const int b = uniform(a.active[i]);
+    // Metadata in two round trips: everything indexed by the layer together
+    // with the active entry, then everything indexed by the request.
+    const int b_raw = gload(a.active + i);
+    const int64_t sbase_raw = gload(a.state_ptrs + l), sstride_raw = gload(a.state_strides + l);
+    const int64_t x_raw = gload(a.x_ptrs + l), xs_raw = gload(a.x_strides + l);
+    const int64_t B_raw = gload(a.B_ptrs + l), Bs_raw = gload(a.B_strides + l);
+    const int64_t dt_raw = gload(a.dt_ptrs + l), dts_raw = gload(a.dt_strides + l);
+    const int64_t A_raw = gload(a.A_ptrs + l);
+    int64_t c_raw = 0, cs_raw = 0;
+    if constexpr (Q) {
+      c_raw = gload(a.scale_ptrs + l);
+      cs_raw = gload(a.scale_strides + l);
+    }
+    const int b = uniform(b_raw);
     const int64_t lb = static_cast<int64_t>(l) * a.B + b;
-    const int s = uniform(a.src_slots[lb]);
+    const int s_raw = gload(a.src_slots + lb);
+    const int r_raw = gload(a.ring_start + b);
+    int d_raw[NCK], k_raw[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+      const int cl = (c < a.ncp) ? c : 0;   // checkpoints past ncp read entry 0 and are then ignored
+      d_raw[c] = gload(a.dst_slots + cl * LB + lb);
+      k_raw[c] = gload(a.prefix_len + static_cast<int64_t>(cl) * a.B + b);
+    }
+    const int s = uniform(s_raw);
     // kc/dc: checkpoints in ascending prefix order (one entry when NCK = 1).
     int kc[NCK], dc[NCK];
     if constexpr (!MULTI) {
-      const int d = uniform(a.dst_slots[lb]);
+      const int d = uniform(d_raw[0]);
       if (s == a.pad || d == a.pad || s < 0 || d < 0) continue;  // pad slot: skipped
-      kc[0] = min(max(uniform(a.prefix_len[b]), 0), a.W);
+      kc[0] = min(max(uniform(k_raw[0]), 0), a.W);
       dc[0] = d;
     } else {
       if (s == a.pad || s < 0) continue;  // pad source: every checkpoint skipped
@@ -378,8 +402,8 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
       for (int c = 0; c < NCK; ++c) {
         int d = a.pad, kk = -1;
         if (c < a.ncp) {
-          d = uniform(a.dst_slots[c * LB + lb]);
-          kk = min(max(uniform(a.prefix_len[static_cast<int64_t>(c) * a.B + b]), 0), a.W);
+          d = uniform(d_raw[c]);
+          kk = min(max(uniform(k_raw[c]), 0), a.W);
         }
         const bool on = d != a.pad && d >= 0;  // a pad destination skips this checkpoint only
         kc[c] = on ? kk : -1;
@@ -389,11 +413,11 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
       if (kc[NCK - 1] < 0) continue;
     }
     const int k = kc[NCK - 1];  // longest prefix
-    int r0 = uniform(a.ring_start[b]) % a.R;
+    int r0 = uniform(r_raw) % a.R;
     if (r0 < 0) r0 += a.R;
 
-    const int64_t sbase = uniform64(a.state_ptrs[l]);
-    const int64_t sstride = uniform64(a.state_strides[l]);
+    const int64_t sbase = uniform64(sbase_raw);
+    const int64_t sstride = uniform64(sstride_raw);
     const char* src_state = reinterpret_cast<const char*>(sbase) + static_cast<int64_t>(s) * sstride * SB;
     char* dst_state[NCK];
 #pragma unroll
@@ -404,8 +428,8 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
 #pragma unroll
     for (int c = 0; c < NCK; ++c) dst_scale[c] = nullptr;
     if constexpr (Q) {
-      const int64_t cbase = uniform64(a.scale_ptrs[l]);
-      const int64_t cstride = uniform64(a.scale_strides[l]);
+      const int64_t cbase = uniform64(c_raw);
+      const int64_t cstride = uniform64(cs_raw);
       src_scale = reinterpret_cast<const float*>(cbase) + static_cast<int64_t>(s) * cstride;
 #pragma unroll
       for (int c = 0; c < NCK; ++c) dst_scale[c] = reinterpret_cast<float*>(cbase) + static_cast<int64_t>(dc[c]) * cstride;
@@ -448,13 +472,13 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
       continue;
     }
 
-    const char* x_slot = reinterpret_cast<const char*>(uniform64(a.x_ptrs[l])) +
-                         static_cast<int64_t>(s) * uniform64(a.x_strides[l]) * IB;
-    const char* B_slot = reinterpret_cast<const char*>(uniform64(a.B_ptrs[l])) +
-                         static_cast<int64_t>(s) * uniform64(a.B_strides[l]) * IB;
-    const float* dt_slot = reinterpret_cast<const float*>(uniform64(a.dt_ptrs[l])) +
-                           static_cast<int64_t>(s) * uniform64(a.dt_strides[l]);
-    const float* A = reinterpret_cast<const float*>(uniform64(a.A_ptrs[l]));
+    const char* x_slot = reinterpret_cast<const char*>(uniform64(x_raw)) +
+                         static_cast<int64_t>(s) * uniform64(xs_raw) * IB;
+    const char* B_slot = reinterpret_cast<const char*>(uniform64(B_raw)) +
+                         static_cast<int64_t>(s) * uniform64(Bs_raw) * IB;
+    const float* dt_slot = reinterpret_cast<const float*>(uniform64(dt_raw)) +
+                           static_cast<int64_t>(s) * uniform64(dts_raw);
+    const float* A = reinterpret_cast<const float*>(uniform64(A_raw));
     const int e_lane = (r0 + lane) % a.R;  // ring entry of token `lane`
     // End of the segment that holds token `lane` (the shortest checkpoint
     // prefix above it); lanes at or past k hold no token.
@@ -469,17 +493,22 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
     }
 
     for (int g = h0 / a.hpg; g * a.hpg < h1; ++g) {
-      // B_j for this lane's 8 columns, shared by the heads of group g.
+      // B_j for this lane's 8 columns, shared by the heads of group g.  All
+      // KMAX rows are requested at once (tokens past k re-read entry r0 and
+      // are then zeroed), so the group costs one round trip, not k.
       float Bv[KMAX][8];
+      {
+        Chunk<IT> braw[KMAX];
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-          const int e = ring_entry(r0, j, a.R);
-          const Chunk<IT> c = load_chunk<IT>(B_slot + ((static_cast<int64_t>(e) * G + g) * DSTATE + cc * 8) * IB);
-          decode_chunk<IT>(c, Bv[j]);
-        } else {
+        for (int j = 0; j < KMAX; ++j) {
+          const int e = ring_entry(r0, j < k ? j : 0, a.R);
+          braw[j] = load_chunk<IT>(B_slot + ((static_cast<int64_t>(e) * G + g) * DSTATE + cc * 8) * IB);
+        }
 #pragma unroll
-          for (int q = 0; q < 8; ++q) Bv[j][q] = 0.0f;
+        for (int j = 0; j < KMAX; ++j) {
+          decode_chunk<IT>(braw[j], Bv[j]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) Bv[j][q] = (j < k) ? Bv[j][q] : 0.0f;
         }
       }
       const int hb = max(h0, g * a.hpg);
@@ -502,6 +531,18 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
 
         // Decay scan: lane j < k holds a_j; suffix products within each
         // segment give the segment decays and the weights w_j.
+        // The head's x rows are requested together with dt and A (one round
+        // trip): lane takes token j = idx / XCH, rows r8 .. r8+7.  Tokens past
+        // k re-read token 0's entry; their values are never used.
+        constexpr int XREP = (KMAX * XCH + 63) / 64;
+        Chunk<IT> xraw[XREP];
+#pragma unroll
+        for (int rep = 0; rep < XREP; ++rep) {
+          const int idx = lane + 64 * rep;
+          const int j = min(idx / XCH, 63);
+          const int ej = __shfl(e_lane, j < k ? j : 0);
+          xraw[rep] = load_chunk<IT>(x_slot + ((static_cast<int64_t>(ej) * a.H + h) * DIM + (idx % XCH) * 8) * IB);
+        }
         const float A_h = gload(A + h);
         float dtj = 0.0f, aj = 1.0f;
         if (lane < k) {
@@ -539,17 +580,15 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
         const int k4 = (k + 3) & ~3;
         wave_lds_fence();
 #pragma unroll
-        for (int rep = 0; rep < (KMAX * XCH + 63) / 64; ++rep) {
+        for (int rep = 0; rep < XREP; ++rep) {
           const int idx = lane + 64 * rep;
           const int j = min(idx / XCH, 63);
           const float wj = __shfl(w, j);
-          const int ej = __shfl(e_lane, j);
           if (idx < k4 * XCH) {
             const int r8 = (idx % XCH) * 8;
             if (j < k) {
               float xv[8];
-              const Chunk<IT> c = load_chunk<IT>(x_slot + ((static_cast<int64_t>(ej) * a.H + h) * DIM + r8) * IB);
-              decode_chunk<IT>(c, xv);
+              decode_chunk<IT>(xraw[rep], xv);
 #pragma unroll
               for (int q = 0; q < 8; ++q) wx[(r8 + q) * KMAX + j] = wj * xv[q];
             } else {
