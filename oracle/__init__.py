@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librssm_oracle.so")
 SRC_PATH = os.path.join(_HERE, "rssm_oracle.c")
 GDN_SRC_PATH = os.path.join(_HERE, "gdn_oracle.c")
+SSU_SRC_PATH = os.path.join(_HERE, "ssu_oracle.c")
 
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3, "f8e4m3": 4, "f64": 5}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "f8e4m3": 1, "f64": 8}
@@ -28,7 +29,7 @@ STORAGE_NP = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16,
 def build(verbose: bool = False) -> str:
     """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", SRC_PATH, GDN_SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
+           "-fPIC", "-shared", SRC_PATH, GDN_SRC_PATH, SSU_SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
@@ -78,6 +79,23 @@ class _GdnOutputs(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("state_out", "exact", "mag")]
 
 
+class _SsuParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_heads", "heads_per_group", "dim", "dstate", "ring_len", "tokens", "pad_slot_id",
+        "state_dtype", "input_dtype", "dt_softplus")]
+
+
+class _SsuInputs(ctypes.Structure):
+    _fields_ = [("state", _VP), ("state_stride", ctypes.c_int64), ("x_ring", _VP), ("x_stride", ctypes.c_int64),
+                ("B_ring", _VP), ("B_stride", ctypes.c_int64), ("dt_ring", _VP), ("dt_stride", ctypes.c_int64),
+                ("A", _VP), ("D", _VP), ("dt_bias", _VP), ("x_new", _VP), ("B_new", _VP), ("C_new", _VP),
+                ("dt_new", _VP), ("z", _VP), ("slots", _VP), ("ring_start", _VP), ("num_buffered", _VP)]
+
+
+class _SsuOutputs(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("x_ring", "B_ring", "dt_ring", "y", "ymag", "dt_exact")]
+
+
 _lib = None
 
 
@@ -108,6 +126,8 @@ def lib():
         L.orc_gdn_tile.argtypes = [_P(_GdnParams), _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
                                    _VP, _VP, _VP, _VP]
         L.orc_gdn_tile.restype = ctypes.c_int
+        L.orc_ssu_decode.argtypes = [_P(_SsuParams), _P(_SsuInputs), _P(_SsuOutputs)]
+        L.orc_ssu_decode.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -341,3 +361,44 @@ def gdn_tile(spec, s0, k_win, v_win, g_win, b_win, n: int, track_step: int = -1)
     if 0 <= track_step < n:
         return fin, finm, trk, trkm
     return fin, finm, None, None
+
+
+# ---------------------------------------------------------------------------
+# ReplaySSM decode step (one layer; see ssu_oracle.h for the readings)
+# ---------------------------------------------------------------------------
+def ssu_decode(prob):
+    """The decode step on a host problem (``rssm_inputs.SsuProblem``).
+    Returns (x_ring, B_ring, dt_ring, y, ymag, dt_exact): the layer's rings
+    after the append (storage dtypes), and fp64 outputs [B, T, H, dim] with
+    their magnitude bounds (NaN for padded requests) and the new tokens' fp64
+    dt [B, T, H]."""
+    spec, pools = prob.spec, prob.pools
+    m = pools.meta
+    p = _SsuParams(batch=spec.B, num_heads=spec.H, heads_per_group=spec.hpg, dim=spec.dim, dstate=spec.dstate,
+                   ring_len=spec.R, tokens=spec.T, pad_slot_id=spec.pad_slot_id,
+                   state_dtype=DTYPE_CODE[spec.state_dtype], input_dtype=DTYPE_CODE[spec.input_dtype],
+                   dt_softplus=1 if spec.dt_softplus else 0)
+    c = lambda a: np.ascontiguousarray(a) if a is not None else None  # noqa: E731
+    arrs = dict(state=c(pools.state[0]), x_ring=c(pools.x[0]), B_ring=c(pools.Bm[0]), dt_ring=c(pools.dt[0]),
+                A=c(prob.A), D=c(prob.D), dt_bias=c(prob.dt_bias), x_new=c(prob.x_new), B_new=c(prob.B_new),
+                C_new=c(prob.C_new), dt_new=c(prob.dt_new), z=c(prob.z),
+                slots=c(prob.slots.astype(np.int32)), ring_start=c(prob.ring_start.astype(np.int32)),
+                num_buffered=c(prob.num_buffered.astype(np.int32)))
+    ptr = lambda k: arrs[k].ctypes.data if arrs[k] is not None else None  # noqa: E731
+    ins = _SsuInputs(state=ptr("state"), state_stride=int(m.state_stride[0]), x_ring=ptr("x_ring"),
+                     x_stride=int(m.x_stride[0]), B_ring=ptr("B_ring"), B_stride=int(m.B_stride[0]),
+                     dt_ring=ptr("dt_ring"), dt_stride=int(m.dt_stride[0]), A=ptr("A"), D=ptr("D"),
+                     dt_bias=ptr("dt_bias"), x_new=ptr("x_new"), B_new=ptr("B_new"), C_new=ptr("C_new"),
+                     dt_new=ptr("dt_new"), z=ptr("z"), slots=ptr("slots"), ring_start=ptr("ring_start"),
+                     num_buffered=ptr("num_buffered"))
+    xr, Br, dtr = arrs["x_ring"].copy(), arrs["B_ring"].copy(), arrs["dt_ring"].copy()
+    shape = (spec.B, spec.T, spec.H, spec.dim)
+    y = np.full(shape, np.nan, np.float64)
+    ym = np.full(shape, np.nan, np.float64)
+    dte = np.full((spec.B, spec.T, spec.H), np.nan, np.float64)
+    outs = _SsuOutputs(x_ring=xr.ctypes.data, B_ring=Br.ctypes.data, dt_ring=dtr.ctypes.data, y=y.ctypes.data,
+                       ymag=ym.ctypes.data, dt_exact=dte.ctypes.data)
+    st = lib().orc_ssu_decode(ctypes.byref(p), ctypes.byref(ins), ctypes.byref(outs))
+    if st != 0:
+        raise OracleError(f"orc_ssu_decode returned {st}")
+    return xr, Br, dtr, y, ym, dte

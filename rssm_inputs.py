@@ -537,3 +537,94 @@ def make_gdn_device_problem(spec: GdnSpec, seed: int, device="cuda", fill: int =
     g = torch.rand((L, S, HV, T), generator=gen, device=device) - 1.0
     beta = torch.sigmoid(torch.randn((L, S, HV, T), generator=gen, device=device))
     return GdnDeviceProblem(spec, state, rawv, rawk, g, beta, idx, acc, tidx, tstep)
+
+
+# --------------------------------------------------------------------------
+# ReplaySSM decode step (one layer): the materialize pools of that layer plus
+# the step's new tokens.
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class SsuSpec:
+    """Shape and structure of one decode-step workload (one layer)."""
+    name: str
+    B: int
+    H: int
+    hpg: int
+    dim: int
+    dstate: int
+    R: int
+    T: int                       # new tokens per request
+    state_dtype: str = "bf16"
+    input_dtype: str = "bf16"
+    has_z: bool = True
+    has_D: bool = True
+    has_bias: bool = True
+    dt_softplus: bool = True
+    slots: int = 0               # state/ring slots (0: 2 * B)
+    pad_frac: float = 0.0        # requests whose slot is the pad slot
+    pad_slot_id: int = -1
+    buffered: Optional[Sequence[int]] = None   # explicit num_buffered, else U[0, R - T]
+
+    @property
+    def G(self) -> int:
+        return self.H // self.hpg
+
+    def pools(self) -> Spec:
+        """The single-layer materialize spec whose pools this step uses."""
+        return Spec(self.name + "_pools", L=1, B=self.B, H=self.H, hpg=self.hpg, dim=self.dim, dstate=self.dstate,
+                    R=self.R, W=min(16, self.R), state_dtype=self.state_dtype, input_dtype=self.input_dtype,
+                    slots=self.slots or 2 * self.B, ring_slots=self.slots or 2 * self.B, slot_mode="perm",
+                    stride_pad="per_layer", pad_slot_id=self.pad_slot_id)
+
+
+SSU_CONFIGS = {
+    "ssu_small": SsuSpec("ssu_small", B=5, H=8, hpg=4, dim=64, dstate=128, R=16, T=4, pad_frac=0.2),
+    # one layer of the large hybrid-model shape, speculative decode with 4 tokens per step
+    "ssu_large": SsuSpec("ssu_large", B=256, H=256, hpg=32, dim=64, dstate=128, R=16, T=4),
+}
+
+
+@dataclasses.dataclass
+class SsuProblem:
+    spec: SsuSpec
+    pools: Problem               # state pool and rings (layer 0)
+    slots: np.ndarray            # (B,) int32 checkpoint/ring slot per request (pad: skipped)
+    ring_start: np.ndarray       # (B,) int32
+    num_buffered: np.ndarray     # (B,) int32
+    A: np.ndarray                # (H,) fp32
+    D: Optional[np.ndarray]      # (H,) fp32
+    dt_bias: Optional[np.ndarray]
+    x_new: np.ndarray            # (B, T, H, dim) input dtype
+    B_new: np.ndarray            # (B, T, G, dstate)
+    C_new: np.ndarray            # (B, T, G, dstate)
+    dt_new: np.ndarray           # (B, T, H) fp32, raw
+    z: Optional[np.ndarray]      # (B, T, H, dim)
+
+
+def make_ssu_problem(spec: SsuSpec, seed: int) -> SsuProblem:
+    """Pools as make_problem (state N(0,1), x N(0,1), B N(0,1/dstate), dt
+    U(0.001, 0.1)); new tokens: x N(0,1), B and C N(0, 1/dstate), z N(0,1),
+    raw dt N(0, 0.3^2) with dt_bias = softplus^-1(U(0.001, 0.1)) (so dt after
+    bias and softplus stays near the ring's range), D U(0.5, 1.5);
+    num_buffered U[0, R - T], ring_start U[0, R)."""
+    rng = np.random.default_rng(seed)
+    pools = make_problem(spec.pools(), seed)
+    B, H, G, T = spec.B, spec.H, spec.G, spec.T
+    slots = pools.meta.src[0].astype(np.int32).copy()
+    if spec.pad_frac > 0:
+        slots[rng.permutation(B)[:int(round(spec.pad_frac * B))]] = spec.pad_slot_id
+    ring_start = pools.meta.ring_start.astype(np.int32).copy()
+    if spec.buffered is not None:
+        nb = np.asarray(spec.buffered, np.int32)
+    else:
+        nb = rng.integers(0, spec.R - T + 1, size=B).astype(np.int32)
+    A = pools.A[0].copy()
+    D = rng.uniform(0.5, 1.5, size=H).astype(np.float32) if spec.has_D else None
+    bias = np.log(np.expm1(rng.uniform(0.001, 0.1, size=H))).astype(np.float32) if spec.has_bias else None
+    x_new = _to_storage(rng.standard_normal((B, T, H, spec.dim), dtype=np.float32), spec.input_dtype)
+    sd = np.float32(1.0 / math.sqrt(spec.dstate))
+    B_new = _to_storage(rng.standard_normal((B, T, G, spec.dstate), dtype=np.float32) * sd, spec.input_dtype)
+    C_new = _to_storage(rng.standard_normal((B, T, G, spec.dstate), dtype=np.float32) * sd, spec.input_dtype)
+    dt_new = (rng.standard_normal((B, T, H)) * 0.3).astype(np.float32)
+    z = _to_storage(rng.standard_normal((B, T, H, spec.dim), dtype=np.float32), spec.input_dtype) if spec.has_z else None
+    return SsuProblem(spec, pools, slots, ring_start, nb, A, D, bias, x_new, B_new, C_new, dt_new, z)
