@@ -129,6 +129,8 @@ def main():
                     help="workload of the profile modes (the headline line always uses large_bf16)")
     ap.add_argument("--only-gdn", action="store_true",
                     help="profile mode: the gated-delta-rule commit line only")
+    ap.add_argument("--only-ssu", action="store_true",
+                    help="profile mode: the decode-step line only")
     ap.add_argument("--only-checkpoints", action="store_true",
                     help="profile mode: the multi-checkpoint line of the large_bf16 workload only")
     ap.add_argument("--no-checkpoints", action="store_true",
@@ -164,6 +166,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.only_gdn:
         print(json.dumps({"gdn_commit": gdn_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
+        return
+    if args.only_ssu:
+        print(json.dumps({"ssu_decode": ssu_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
         return
     profile_mode = args.only_main or args.empty_only or args.pmc_calibrate or args.only_checkpoints
     wl = args.workload if profile_mode else WORKLOAD
@@ -332,6 +337,7 @@ def main():
         result["other_workloads"] = {name: other_workload(name, dev, stream, max(5, args.steps // 2))
                                      for name in ("large_i8", "large_f8sr")}
         result["other_workloads"]["gdn_commit"] = gdn_workload(dev, stream, max(5, args.steps // 2))
+        result["other_workloads"]["ssu_decode"] = ssu_workload(dev, stream, max(5, args.steps // 2))
     print(json.dumps(result), flush=True)
 
 
@@ -408,6 +414,39 @@ def gdn_workload(dev, stream, steps):
            "us_per_request": round(ms * 1e3 / max(live, 1), 3)}
     say(f"gdn_commit: {out}")
     del call, dp, meta
+    torch.cuda.empty_cache()
+    return out
+
+
+def ssu_workload(dev, stream, steps):
+    """The decode step on ssu_large (one layer): 256 requests, 256 heads in 8
+    groups, 64x128 bf16 checkpoints, bf16 inputs, ring of 16 with U[0, 12]
+    pending entries, 4 new tokens per request (speculative decode), D, dt_bias
+    and the z gate.  The checkpoint is read only and the append rewrites the
+    same ring entries, so every timed call does identical work."""
+    import torch
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    spec = ri.SSU_CONFIGS["ssu_large"]
+    seed = 1020
+    say("generating ssu_large seed", seed)
+    dp = ri.make_ssu_device_problem(spec, seed, dev)
+    call = hx.ssu_prepared(dp)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ms = timed_calls(call, steps, stream)
+    nbytes = hx.ssu_bytes(spec, dp.slots_np, dp.num_buffered_np)
+    live = int((dp.slots_np != spec.pad_slot_id).sum())
+    out = {"workload": f"ssu_large: B={spec.B} ({live} live), H={spec.H} (hpg {spec.hpg}), {spec.dim}x{spec.dstate} "
+                       f"{spec.state_dtype} checkpoints, {spec.input_dtype} inputs, R={spec.R}, T={spec.T} new "
+                       f"tokens, mean {float(dp.num_buffered_np.mean()):.2f} pending",
+           "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+           "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "us_per_request": round(ms * 1e3 / max(live, 1), 3)}
+    say(f"ssu_decode: {out}")
+    del call, dp
     torch.cuda.empty_cache()
     return out
 

@@ -10,4 +10,5 @@ from ._binding import (  # noqa: F401
     checkpoint_prefix_len, dtype_code, lib, make_desc, pointer_table, replayssm_materialize,
     rssm_debug_encode_rows, rssm_last_error, rssm_materialize, rssm_materialize_checkpoints,
     rssm_materialize_launch_config, RSSM_MAX_CHECKPOINTS, stride_table, rssm_gdn_commit,
-    gated_delta_rule_replayssm_commit, GdnCommitCall, RssmGdnDesc, RssmGdnTables)
+    gated_delta_rule_replayssm_commit, GdnCommitCall, RssmGdnDesc, RssmGdnTables, rssm_ssu_decode,
+    SsuDecodeCall, RssmSsuDesc, RssmSsuTables, RSSM_SSU_MAX_TOKENS, RSSM_SSU_MAX_REPLAY)

@@ -18,8 +18,10 @@ LIB_PATH = os.path.join(_PKG, "librssm_materialize.so")
 RSSM_F32, RSSM_BF16, RSSM_F16, RSSM_I8, RSSM_F8E4M3 = 0, 1, 2, 3, 4
 RSSM_OK, RSSM_ERR_INVALID_ARGUMENT, RSSM_ERR_UNSUPPORTED, RSSM_ERR_HIP = 0, 1, 2, 3
 EXPORTS = ("rssm_materialize", "rssm_materialize_checkpoints", "rssm_last_error", "rssm_materialize_launch_config",
-           "rssm_debug_encode_rows", "rssm_gdn_commit")
+           "rssm_debug_encode_rows", "rssm_gdn_commit", "rssm_ssu_decode")
 RSSM_MAX_CHECKPOINTS = 4
+RSSM_SSU_MAX_TOKENS = 8
+RSSM_SSU_MAX_REPLAY = 16
 _INT32_MAX = 2**31 - 1
 
 
@@ -61,6 +63,19 @@ class RssmGdnTables(ctypes.Structure):
         "track_state_indices", "track_steps")]
 
 
+class RssmSsuDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_heads", "heads_per_group", "dim", "dstate", "ring_buffer_len", "tokens", "num_slots",
+        "pad_slot_id", "state_dtype", "input_dtype", "dt_softplus", "max_workgroups")] + [
+        (n, ctypes.c_int64) for n in ("state_slot_stride", "x_slot_stride", "B_slot_stride", "dt_slot_stride")]
+
+
+class RssmSsuTables(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "state", "x_ring", "B_ring", "dt_ring", "A", "D", "dt_bias", "x_new", "B_new", "C_new", "dt_new", "z", "y",
+        "slots", "ring_start", "num_buffered")]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -74,6 +89,8 @@ def _load():
     lib.rssm_materialize_checkpoints.restype = ctypes.c_int
     lib.rssm_gdn_commit.argtypes = [ctypes.POINTER(RssmGdnDesc), ctypes.POINTER(RssmGdnTables), ctypes.c_void_p]
     lib.rssm_gdn_commit.restype = ctypes.c_int
+    lib.rssm_ssu_decode.argtypes = [ctypes.POINTER(RssmSsuDesc), ctypes.POINTER(RssmSsuTables), ctypes.c_void_p]
+    lib.rssm_ssu_decode.restype = ctypes.c_int
     lib.rssm_last_error.argtypes = []
     lib.rssm_last_error.restype = ctypes.c_char_p
     lib.rssm_materialize_launch_config.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(ctypes.c_int32),
@@ -347,6 +364,74 @@ class GdnCommitCall:
 
     def __call__(self) -> None:
         st = _lib.rssm_gdn_commit(self._refs[0], self._refs[1], self._stream)
+        if st != RSSM_OK:
+            raise RssmError(st, rssm_last_error())
+
+
+def _slot_stride(t, name: str, slots: int) -> int:
+    if t.dim() < 2 or int(t.shape[0]) != slots:
+        raise ValueError(f"{name} must be a pool with one row per slot ({slots} slots; got shape {tuple(t.shape)})")
+    return t.numel() // slots
+
+
+def _ssu_marshal(state, x_ring, B_ring, dt_ring, A, x_new, B_new, C_new, dt_new, y, slots, ring_start,
+                 num_buffered, *, ring_buffer_len: int, D=None, dt_bias=None, z=None, dt_softplus: bool = True,
+                 pad_slot_id: int = -1, max_workgroups: int = 0):
+    import torch
+    if x_new.dim() != 4 or C_new.dim() != 4:
+        raise ValueError("x_new must be [B, T, H, dim] and C_new [B, T, G, dstate]")
+    B, T, H, dim = (int(v) for v in x_new.shape)
+    G, dstate = int(C_new.shape[2]), int(C_new.shape[3])
+    if G < 1 or H % G != 0:
+        raise ValueError(f"the group count of C_new ({G}) must divide the head count ({H})")
+    S = int(state.shape[0])
+    f32, i32, idt = torch.float32, torch.int32, x_new.dtype
+    desc = RssmSsuDesc(
+        batch=_scalar("batch", B), num_heads=_scalar("num_heads", H), heads_per_group=_scalar("hpg", H // G),
+        dim=_scalar("dim", dim), dstate=_scalar("dstate", dstate),
+        ring_buffer_len=_scalar("ring_buffer_len", ring_buffer_len), tokens=_scalar("tokens", T),
+        num_slots=_scalar("num_slots", S), pad_slot_id=_scalar("pad_slot_id", pad_slot_id),
+        state_dtype=dtype_code(state.dtype), input_dtype=dtype_code(idt), dt_softplus=1 if dt_softplus else 0,
+        max_workgroups=_scalar("max_workgroups", max_workgroups),
+        state_slot_stride=_slot_stride(state, "state", S), x_slot_stride=_slot_stride(x_ring, "x_ring", S),
+        B_slot_stride=_slot_stride(B_ring, "B_ring", S), dt_slot_stride=_slot_stride(dt_ring, "dt_ring", S))
+    tab = RssmSsuTables(
+        state=_ptr(state, "state"), x_ring=_ptr(x_ring, "x_ring", idt), B_ring=_ptr(B_ring, "B_ring", idt),
+        dt_ring=_ptr(dt_ring, "dt_ring", f32), A=_ptr(A, "A", f32, (H,)), D=_ptr(D, "D", f32, (H,)),
+        dt_bias=_ptr(dt_bias, "dt_bias", f32, (H,)), x_new=_ptr(x_new, "x_new", idt),
+        B_new=_ptr(B_new, "B_new", idt, (B, T, G, dstate)), C_new=_ptr(C_new, "C_new", idt),
+        dt_new=_ptr(dt_new, "dt_new", f32, (B, T, H)), z=_ptr(z, "z", idt, (B, T, H, dim)),
+        y=_ptr(y, "y", f32, (B, T, H, dim)), slots=_ptr(slots, "slots", i32, (B,)),
+        ring_start=_ptr(ring_start, "ring_start", i32, (B,)), num_buffered=_ptr(num_buffered, "num_buffered", i32, (B,)))
+    return desc, tab
+
+
+def rssm_ssu_decode(*args, stream=None, **kw) -> None:
+    """Enqueue one ReplaySSM decode step (one layer): the outputs y (fp32 [B,
+    T, H, dim]) of T new tokens read from checkpoint + ring + the new tokens,
+    which are appended to the ring; the checkpoint is not written.
+    Positional: state pool [slots, ...] (f32/bf16/f16), x_ring / B_ring pools
+    [slots, ...] (input dtype), dt_ring pool [slots, ...] fp32, A fp32 [H],
+    x_new [B, T, H, dim], B_new / C_new [B, T, G, dstate], dt_new fp32 [B, T,
+    H] (raw), y, slots / ring_start / num_buffered int32 [B].  Pools are
+    contiguous with one row per slot; the slot stride is the row size.
+    Keywords: ring_buffer_len (required), D, dt_bias, z (optional),
+    dt_softplus=True, pad_slot_id=-1, max_workgroups=0."""
+    desc, tab = _ssu_marshal(*args, **kw)
+    _check(_lib.rssm_ssu_decode(ctypes.byref(desc), ctypes.byref(tab), _stream_handle(stream)))
+
+
+class SsuDecodeCall:
+    """A prepared rssm_ssu_decode: arguments checked and marshalled once; each
+    call is one C call.  stream=None binds torch's current stream."""
+
+    def __init__(self, *args, stream=None, **kw):
+        self._desc, self._tab = _ssu_marshal(*args, **kw)
+        self._refs = (ctypes.byref(self._desc), ctypes.byref(self._tab))
+        self._stream = _stream_handle(stream)
+
+    def __call__(self) -> None:
+        st = _lib.rssm_ssu_decode(self._refs[0], self._refs[1], self._stream)
         if st != RSSM_OK:
             raise RssmError(st, rssm_last_error())
 

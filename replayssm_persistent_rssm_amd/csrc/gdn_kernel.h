@@ -51,16 +51,6 @@ struct GdnArgs {
 
 constexpr int kGdnDim = 128;   // key and value width, fixed by the page
 
-// Sum over the 16 lanes of an aligned lane group (the same exchange pattern
-// as row16_max).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  v += dpp<0x140>(v);  // row_mirror
-  return v;
-}
-
 // Register budget: the keys cost 8 * TMAX registers per lane.
 template <int TMAX> constexpr int kGdnWavesPerSimd = (TMAX > 8) ? 2 : 3;
 

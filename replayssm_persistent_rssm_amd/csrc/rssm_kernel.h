@@ -116,6 +116,16 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Sum over the 16 lanes of an aligned lane group, every lane receiving the
+// total (the same exchange pattern as row16_max).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
 // Encode this lane's 8 fp32 values of one state row.  One-byte state reduces
 // the row max over the row's 16 lanes (all 64 lanes must execute this) and
 // returns the new row scale in `row_scale`.

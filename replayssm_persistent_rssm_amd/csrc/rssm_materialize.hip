@@ -11,6 +11,7 @@
 // overflow).  Device metadata is never read on the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdint>
@@ -24,6 +25,8 @@
 #include "rssm_gdn_commit.h"
 #include "rssm_kernel.h"
 #include "rssm_materialize.h"
+#include "rssm_ssu_decode.h"
+#include "ssu_kernel.h"
 
 namespace rssm {
 const KernelEntry* kernels_f32(int* n);
@@ -37,6 +40,7 @@ const EncodeEntry* encoders_f16(int* n);
 const EncodeEntry* encoders_i8(int* n);
 const EncodeEntry* encoders_f8(int* n);
 const void* gdn_kernel_for(int window);
+const void* ssu_kernel_for(int state_dtype, int input_dtype, int tokens);
 }  // namespace rssm
 
 namespace {
@@ -443,6 +447,116 @@ rssm_status rssm_gdn_commit(const rssm_gdn_commit_desc* d, const rssm_gdn_commit
   void* params[] = {&args};
   hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(rssm::kBlock), params, 0, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(RSSM_ERR_HIP, "launch of gdn_commit failed: %s", hipGetErrorString(e));
+  return RSSM_OK;
+}
+
+rssm_status rssm_ssu_decode(const rssm_ssu_decode_desc* d, const rssm_ssu_decode_tables* t, void* hip_stream) {
+  g_err[0] = '\0';
+  if (d == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 0) return fail(RSSM_ERR_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", d->batch);
+  if (d->num_heads < 1) return fail(RSSM_ERR_INVALID_ARGUMENT, "num_heads must be >= 1 (got %d)", d->num_heads);
+  if (d->heads_per_group < 1 || d->num_heads % d->heads_per_group != 0)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "heads_per_group (%d) must be >= 1 and divide num_heads (%d)",
+                d->heads_per_group, d->num_heads);
+  if (d->tokens < 1 || d->tokens > RSSM_SSU_MAX_TOKENS)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "tokens must be in [1, %d] (got %d)", RSSM_SSU_MAX_TOKENS, d->tokens);
+  if (d->ring_buffer_len < d->tokens)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "ring_buffer_len (%d) must be >= tokens (%d)", d->ring_buffer_len,
+                d->tokens);
+  if (d->num_slots < 1) return fail(RSSM_ERR_INVALID_ARGUMENT, "num_slots must be >= 1 (got %d)", d->num_slots);
+  if (d->dt_softplus != 0 && d->dt_softplus != 1)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "dt_softplus must be 0 or 1 (got %d)", d->dt_softplus);
+  if (d->max_workgroups < 0)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "max_workgroups must be >= 0 (got %d)", d->max_workgroups);
+  for (int dt : {d->state_dtype, d->input_dtype})
+    if (dt < RSSM_F32 || dt > RSSM_F8E4M3) return fail(RSSM_ERR_INVALID_ARGUMENT, "unknown dtype %d", dt);
+  if (d->state_dtype > RSSM_F16 || d->input_dtype > RSSM_F16)
+    return fail(RSSM_ERR_UNSUPPORTED, "state and input dtypes must be f32, bf16 or f16 (got %s, %s)",
+                dtype_name(d->state_dtype), dtype_name(d->input_dtype));
+  if (d->dim != rssm::kSsuDim || d->dstate != rssm::kSsuDstate)
+    return fail(RSSM_ERR_UNSUPPORTED, "no compiled instance for dim=%d dstate=%d (64, 128)", d->dim, d->dstate);
+  const int64_t H = d->num_heads, G = H / d->heads_per_group, R = d->ring_buffer_len;
+  const int64_t sb = (d->state_dtype == RSSM_F32) ? 4 : 2, ib = (d->input_dtype == RSSM_F32) ? 4 : 2;
+  // 32-bit byte offsets inside one slot's x ring
+  if (R * H * d->dim * ib > (int64_t(1) << 31))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "ring_buffer_len*num_heads*dim*element size exceeds 2^31 bytes");
+  if (H > (int64_t(1) << 24)) return fail(RSSM_ERR_INVALID_ARGUMENT, "num_heads exceeds 2^24");
+  if (static_cast<int64_t>(d->batch) * d->tokens * H * d->dim > (int64_t(1) << 46))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "batch*tokens*num_heads*dim exceeds 2^46");
+  if (d->state_slot_stride < H * d->dim * d->dstate || d->x_slot_stride < R * H * d->dim ||
+      d->B_slot_stride < R * G * d->dstate || d->dt_slot_stride < R * H)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "a slot stride is below the dense per-slot size");
+  if ((d->state_slot_stride * sb) % 16 != 0 || (d->B_slot_stride * ib) % 16 != 0)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "state and B slot strides must be multiples of 16 bytes");
+  const int64_t max_stride = std::max(std::max(d->state_slot_stride, d->x_slot_stride),
+                                      std::max(d->B_slot_stride, d->dt_slot_stride));
+  if (static_cast<int64_t>(d->num_slots) * max_stride > (int64_t(1) << 46))
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "num_slots*slot stride exceeds 2^46 elements");
+  if (t == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "tables is NULL");
+  if (d->batch == 0) return RSSM_OK;   // nothing to enqueue; empty tensors may have NULL addresses
+  struct P { const void* p; const char* n; int align; };
+  const P ptrs[] = {{t->state, "state", 16},       {t->x_ring, "x_ring", static_cast<int>(ib)},
+                    {t->B_ring, "B_ring", 16},     {t->dt_ring, "dt_ring", 4},
+                    {t->A, "A", 4},                {t->x_new, "x_new", static_cast<int>(ib)},
+                    {t->B_new, "B_new", 16},       {t->C_new, "C_new", 16},
+                    {t->dt_new, "dt_new", 4},      {t->y, "y", 4},
+                    {t->slots, "slots", 4},        {t->ring_start, "ring_start", 4},
+                    {t->num_buffered, "num_buffered", 4}};
+  for (const P& e : ptrs) {
+    if (e.p == nullptr) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is NULL", e.n);
+    if (!aligned(e.p, e.align)) return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", e.n, e.align);
+  }
+  const P opt[] = {{t->D, "D", 4}, {t->dt_bias, "dt_bias", 4}, {t->z, "z", static_cast<int>(ib)}};
+  for (const P& e : opt)
+    if (e.p != nullptr && !aligned(e.p, e.align))
+      return fail(RSSM_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", e.n, e.align);
+  const void* fn = rssm::ssu_kernel_for(d->state_dtype, d->input_dtype, d->tokens);
+  if (fn == nullptr) return fail(RSSM_ERR_UNSUPPORTED, "no decode-step instance for these dtypes and tokens");
+  int grid = d->max_workgroups;
+  if (grid == 0) {
+    rssm_status st = grid_for(fn, &grid);
+    if (st != RSSM_OK) return st;
+  }
+  rssm::SsuArgs args;
+  args.state = static_cast<const char*>(t->state);
+  args.x_ring = static_cast<char*>(t->x_ring);
+  args.B_ring = static_cast<char*>(t->B_ring);
+  args.dt_ring = t->dt_ring;
+  args.A = t->A;
+  // absent optional vectors: the kernel reads A in their place and ignores it
+  args.D = t->D != nullptr ? t->D : t->A;
+  args.dt_bias = t->dt_bias != nullptr ? t->dt_bias : t->A;
+  args.x_new = static_cast<const char*>(t->x_new);
+  args.B_new = static_cast<const char*>(t->B_new);
+  args.C_new = static_cast<const char*>(t->C_new);
+  args.dt_new = t->dt_new;
+  args.z = static_cast<const char*>(t->z != nullptr ? t->z : t->x_new);
+  args.y = t->y;
+  args.slots = t->slots;
+  args.ring_start = t->ring_start;
+  args.num_buffered = t->num_buffered;
+  args.state_stride = d->state_slot_stride;
+  args.x_stride = d->x_slot_stride;
+  args.B_stride = d->B_slot_stride;
+  args.dt_stride = d->dt_slot_stride;
+  args.B = d->batch;
+  args.H = d->num_heads;
+  args.hpg = d->heads_per_group;
+  args.R = d->ring_buffer_len;
+  args.T = d->tokens;
+  args.pad = d->pad_slot_id;
+  args.num_slots = d->num_slots;
+  args.dt_softplus = d->dt_softplus;
+  args.has_D = t->D != nullptr;
+  args.has_bias = t->dt_bias != nullptr;
+  args.has_z = t->z != nullptr;
+  if (verbose())
+    std::fprintf(stderr, "[rssm_ssu_decode] %s/%s tokens<=%d grid=%d block=%d B=%d H=%d\n",
+                 dtype_name(d->state_dtype), dtype_name(d->input_dtype), d->tokens <= 4 ? 4 : 8, grid,
+                 rssm::kBlock, d->batch, d->num_heads);
+  void* params[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(rssm::kBlock), params, 0, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(RSSM_ERR_HIP, "launch of ssu_decode failed: %s", hipGetErrorString(e));
   return RSSM_OK;
 }
 

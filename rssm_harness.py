@@ -211,3 +211,65 @@ def gdn_bytes(spec: ri.GdnSpec, idx, acc, tidx=None, tstep=None) -> int:
         per_head = 2 * tile + (tile if tracked else 0) + n * (spec.dv * 2 + 8)
         total += spec.L * (spec.HV * per_head + spec.H * n * spec.dk * 2)
     return total
+
+
+# --------------------------------------------------------------------------
+# Decode step
+# --------------------------------------------------------------------------
+def _ssu_args(d: ri.SsuDeviceProblem, max_workgroups: int = 0):
+    spec = d.spec
+    args = (d.state, d.x_ring, d.B_ring, d.dt_ring, d.A, d.x_new, d.B_new, d.C_new, d.dt_new, d.y, d.slots,
+            d.ring_start, d.num_buffered)
+    kw = dict(ring_buffer_len=spec.R, D=d.D, dt_bias=d.dt_bias, z=d.z, dt_softplus=spec.dt_softplus,
+              pad_slot_id=spec.pad_slot_id, max_workgroups=max_workgroups)
+    return args, kw
+
+
+def ssu_call(d: ri.SsuDeviceProblem, max_workgroups: int = 0, stream=None) -> None:
+    """One rssm_ssu_decode call on a device problem (enqueued, not synchronised)."""
+    import replayssm_persistent_rssm_amd as rp
+    args, kw = _ssu_args(d, max_workgroups)
+    rp.rssm_ssu_decode(*args, stream=stream, **kw)
+
+
+def ssu_prepared(d: ri.SsuDeviceProblem, max_workgroups: int = 0, stream=None):
+    """The same call, marshalled once (a callable that makes one C call)."""
+    import replayssm_persistent_rssm_amd as rp
+    args, kw = _ssu_args(d, max_workgroups)
+    return rp.SsuDecodeCall(*args, stream=stream, **kw)
+
+
+def _host_storage(t, dtype: str) -> np.ndarray:
+    import torch
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def ssu_download(d: ri.SsuDeviceProblem):
+    """(x_ring, B_ring, dt_ring, y) in host storage form after a call."""
+    it = d.spec.input_dtype
+    return (_host_storage(d.x_ring, it), _host_storage(d.B_ring, it), d.dt_ring.cpu().numpy(), d.y.cpu().numpy())
+
+
+def ssu_bytes(spec: ri.SsuSpec, slots, num_buffered) -> int:
+    """Bytes a decode step must move: per live request the checkpoint tiles
+    (read), the n pending ring entries (x, dt per head; B per group; read),
+    the T new tokens' inputs (x, z, dt per head; B, C per group; read), the
+    outputs (fp32, written) and the ring append (x, dt per head; B per group;
+    written); plus A, D and dt_bias once."""
+    sb = {"f32": 4, "bf16": 2, "f16": 2}[spec.state_dtype]
+    ib = {"f32": 4, "bf16": 2, "f16": 2}[spec.input_dtype]
+    H, G, T, dim, ds = spec.H, spec.G, spec.T, spec.dim, spec.dstate
+    x_row, b_row = dim * ib, ds * ib
+    total = 3 * H * 4
+    for b in range(spec.B):
+        if int(slots[b]) == spec.pad_slot_id:
+            continue
+        n = int(num_buffered[b])
+        total += H * dim * ds * sb                                       # checkpoint
+        total += n * (H * (x_row + 4) + G * b_row)                       # pending entries
+        total += T * (H * (x_row * (2 if spec.has_z else 1) + 4) + 2 * G * b_row)   # new inputs
+        total += T * H * dim * 4                                         # outputs
+        total += T * (H * (x_row + 4) + G * b_row)                       # ring append
+    return total

@@ -628,3 +628,92 @@ def make_ssu_problem(spec: SsuSpec, seed: int) -> SsuProblem:
     dt_new = (rng.standard_normal((B, T, H)) * 0.3).astype(np.float32)
     z = _to_storage(rng.standard_normal((B, T, H, spec.dim), dtype=np.float32), spec.input_dtype) if spec.has_z else None
     return SsuProblem(spec, pools, slots, ring_start, nb, A, D, bias, x_new, B_new, C_new, dt_new, z)
+
+
+@dataclasses.dataclass
+class SsuDeviceProblem:
+    """A decode-step problem in device memory (torch tensors; 16-bit float
+    storage as torch.bfloat16 / torch.float16)."""
+    spec: SsuSpec
+    state: object            # (slots, state_stride) state dtype
+    x_ring: object           # (slots, x_stride) input dtype
+    B_ring: object           # (slots, B_stride)
+    dt_ring: object          # (slots, dt_stride) fp32
+    A: object
+    D: Optional[object]
+    dt_bias: Optional[object]
+    x_new: object
+    B_new: object
+    C_new: object
+    dt_new: object
+    z: Optional[object]
+    y: object                # (B, T, H, dim) fp32, NaN-filled
+    slots: object            # (B,) int32 device
+    ring_start: object
+    num_buffered: object
+    slots_np: np.ndarray
+    ring_start_np: np.ndarray
+    num_buffered_np: np.ndarray
+
+
+def _torch_typed(a: np.ndarray, dtype: str, device):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def ssu_to_device(prob: SsuProblem, device="cuda") -> SsuDeviceProblem:
+    """Copy a host decode-step problem to the device, same layouts."""
+    import torch
+    spec, pools = prob.spec, prob.pools
+    it = spec.input_dtype
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device) if a is not None else None  # noqa: E731
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)  # noqa: E731
+    y = torch.full((spec.B, spec.T, spec.H, spec.dim), float("nan"), dtype=torch.float32, device=device)
+    return SsuDeviceProblem(
+        spec=spec, state=_torch_typed(pools.state[0], spec.state_dtype, device),
+        x_ring=_torch_typed(pools.x[0], it, device), B_ring=_torch_typed(pools.Bm[0], it, device),
+        dt_ring=f(pools.dt[0]), A=f(prob.A), D=f(prob.D), dt_bias=f(prob.dt_bias),
+        x_new=_torch_typed(prob.x_new, it, device), B_new=_torch_typed(prob.B_new, it, device),
+        C_new=_torch_typed(prob.C_new, it, device), dt_new=f(prob.dt_new),
+        z=_torch_typed(prob.z, it, device) if prob.z is not None else None, y=y,
+        slots=i32(prob.slots), ring_start=i32(prob.ring_start), num_buffered=i32(prob.num_buffered),
+        slots_np=prob.slots.astype(np.int32), ring_start_np=prob.ring_start.astype(np.int32),
+        num_buffered_np=prob.num_buffered.astype(np.int32))
+
+
+def make_ssu_device_problem(spec: SsuSpec, seed: int, device="cuda") -> SsuDeviceProblem:
+    """Full-size decode-step problem drawn on the device (seeded torch
+    generator) with the distributions of make_ssu_problem; the pools are
+    make_device_problem's (request slots random, every other slot's state
+    filled with the byte 0xA5)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    pools = make_device_problem(spec.pools(), seed, device)
+    B, H, G, T = spec.B, spec.H, spec.G, spec.T
+    slots = pools.meta.src[0].astype(np.int32).copy()
+    if spec.pad_frac > 0:
+        slots[rng.permutation(B)[:int(round(spec.pad_frac * B))]] = spec.pad_slot_id
+    ring_start = pools.meta.ring_start.astype(np.int32).copy()
+    if spec.buffered is not None:
+        nb = np.asarray(spec.buffered, np.int32)
+    else:
+        nb = rng.integers(0, spec.R - T + 1, size=B).astype(np.int32)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 1)
+    idt = _torch_storage(spec.input_dtype)
+    sd = 1.0 / math.sqrt(spec.dstate)
+    rn = lambda *shape: torch.randn(shape, generator=g, device=device, dtype=torch.float32)  # noqa: E731
+    D = torch.from_numpy(rng.uniform(0.5, 1.5, size=H).astype(np.float32)).to(device) if spec.has_D else None
+    bias = (torch.from_numpy(np.log(np.expm1(rng.uniform(0.001, 0.1, size=H))).astype(np.float32)).to(device)
+            if spec.has_bias else None)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)  # noqa: E731
+    y = torch.full((B, T, H, spec.dim), float("nan"), dtype=torch.float32, device=device)
+    return SsuDeviceProblem(
+        spec=spec, state=pools.state[0], x_ring=pools.x[0], B_ring=pools.Bm[0], dt_ring=pools.dt[0], A=pools.A[0],
+        D=D, dt_bias=bias, x_new=rn(B, T, H, spec.dim).to(idt), B_new=rn(B, T, G, spec.dstate).mul_(sd).to(idt),
+        C_new=rn(B, T, G, spec.dstate).mul_(sd).to(idt), dt_new=rn(B, T, H).mul_(0.3),
+        z=rn(B, T, H, spec.dim).to(idt) if spec.has_z else None, y=y, slots=i32(slots), ring_start=i32(ring_start),
+        num_buffered=i32(nb), slots_np=slots, ring_start_np=ring_start, num_buffered_np=nb)

@@ -220,3 +220,72 @@ def test_gdn_tables_rejected(rp):
     assert "track" in rp.rssm_last_error()
     # an empty batch enqueues nothing and touches no device
     assert rp.lib().rssm_gdn_commit(ctypes.byref(_gdn_desc(rp, batch=0)), ctypes.byref(_gdn_tables(rp)), None) == 0
+
+
+def _ssu_desc(rp, **kw):
+    H, R = 256, 16
+    base = dict(batch=256, num_heads=H, heads_per_group=32, dim=64, dstate=128, ring_buffer_len=R, tokens=4,
+                num_slots=512, pad_slot_id=-1, state_dtype=1, input_dtype=1, dt_softplus=1, max_workgroups=0,
+                state_slot_stride=H * 64 * 128, x_slot_stride=R * H * 64, B_slot_stride=R * 8 * 128,
+                dt_slot_stride=R * H)
+    base.update(kw)
+    return rp.RssmSsuDesc(**base)
+
+
+def _ssu_tables(rp, **override):
+    t = rp.RssmSsuTables(**{f: 0x10000 for f, _ in rp.RssmSsuTables._fields_})
+    for k, v in override.items():
+        setattr(t, k, v)
+    return t
+
+
+BAD_SSU = [
+    (dict(batch=-1), 1, "batch"), (dict(num_heads=0), 1, "num_heads"), (dict(heads_per_group=3), 1, "divide"),
+    (dict(tokens=0), 1, "tokens"), (dict(tokens=9), 1, "tokens"), (dict(ring_buffer_len=3), 1, "ring_buffer_len"),
+    (dict(num_slots=0), 1, "num_slots"), (dict(dt_softplus=2), 1, "dt_softplus"),
+    (dict(max_workgroups=-1), 1, "max_workgroups"), (dict(state_dtype=7), 1, "dtype"),
+    (dict(state_dtype=3), 2, "f32, bf16 or f16"), (dict(input_dtype=4), 2, "f32, bf16 or f16"),
+    (dict(dim=16, dstate=16), 2, "dim=16"), (dict(state_slot_stride=100), 1, "stride"),
+    (dict(x_slot_stride=16 * 256 * 64 - 1), 1, "stride"), (dict(state_slot_stride=256 * 64 * 128 + 3), 1, "16 bytes"),
+    (dict(ring_buffer_len=2**20, x_slot_stride=2**20 * 256 * 64, dt_slot_stride=2**20 * 256,
+          B_slot_stride=2**20 * 8 * 128), 1, "2^31"),
+]
+
+
+@pytest.mark.parametrize("kw,status,text", BAD_SSU)
+def test_ssu_bad_scalars_rejected(rp, kw, status, text):
+    d = _ssu_desc(rp, **kw)
+    assert rp.lib().rssm_ssu_decode(ctypes.byref(d), ctypes.byref(_ssu_tables(rp)), None) == status
+    assert text in rp.rssm_last_error()
+
+
+def test_ssu_tables_rejected(rp):
+    d = _ssu_desc(rp)
+    assert rp.lib().rssm_ssu_decode(ctypes.byref(d), None, None) == 1
+    assert rp.lib().rssm_ssu_decode(None, None, None) == 1
+    for field in ("state", "x_ring", "B_ring", "dt_ring", "A", "x_new", "B_new", "C_new", "dt_new", "y", "slots",
+                  "ring_start", "num_buffered"):
+        t = _ssu_tables(rp, **{field: None})
+        assert rp.lib().rssm_ssu_decode(ctypes.byref(d), ctypes.byref(t), None) == 1
+        assert field in rp.rssm_last_error()
+    for field in ("state", "B_ring", "C_new"):
+        t = _ssu_tables(rp, **{field: 0x10008})
+        assert rp.lib().rssm_ssu_decode(ctypes.byref(d), ctypes.byref(t), None) == 1
+        assert "aligned" in rp.rssm_last_error()
+    t = _ssu_tables(rp, z=0x10001)
+    assert rp.lib().rssm_ssu_decode(ctypes.byref(d), ctypes.byref(t), None) == 1
+    # the optional vectors may be absent; an empty batch enqueues nothing and touches no device
+    t = _ssu_tables(rp, D=None, dt_bias=None, z=None, x_new=None, y=None)
+    assert rp.lib().rssm_ssu_decode(ctypes.byref(_ssu_desc(rp, batch=0)), ctypes.byref(t), None) == 0
+
+
+def test_ssu_byte_count():
+    """The decode step's algorithmic bytes, written out for one live request
+    with n = 3 and one padded request."""
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    spec = ri.with_(ri.SSU_CONFIGS["ssu_small"], B=2, T=2, has_z=True)
+    H, G, T, dim, ds = spec.H, spec.G, spec.T, spec.dim, spec.dstate
+    want = 3 * H * 4 + H * dim * ds * 2 + 3 * (H * (dim * 2 + 4) + G * ds * 2)
+    want += T * (H * (2 * dim * 2 + 4) + 2 * G * ds * 2) + T * H * dim * 4 + T * (H * (dim * 2 + 4) + G * ds * 2)
+    assert hx.ssu_bytes(spec, [7, spec.pad_slot_id], [3, 5]) == want
