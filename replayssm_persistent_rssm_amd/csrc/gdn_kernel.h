@@ -15,9 +15,10 @@
 // Design (MI355X, wave64):
 //  * The update never mixes rows of S: row i evolves by its own dot product
 //    with the token's key.  So a state tile is streamed row-wise, like the
-//    materialize kernel's: 16 lanes per row, 8 key columns per lane, 4 rows
-//    per wavefront pass, PD passes in flight while earlier passes run their
-//    tokens.  Work item = one (request, layer, value head) tile; tiles are
+//    materialize kernel's: 16 lanes per row, 8 key columns per lane (two
+//    halves, 4*cc.. and 64 + 4*cc.., so that every 16-byte access instruction
+//    is contiguous across the lanes of a row), 4 rows per wavefront pass, PD
+//    passes in flight while earlier passes run their tokens.  Work item = one (request, layer, value head) tile; tiles are
 //    dealt round-robin over the wavefronts, so each sees the same mix of
 //    cheap (skipped), plain and tracked requests.  No workgroup barriers.
 //  * The normalised keys live in registers (8 columns x up to TMAX tokens per
@@ -87,7 +88,7 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
   float* vw = lds_v[wave];
   const int cc = lane % TPR;
   const int rr = lane / TPR;
-  const uint32_t lane_off = static_cast<uint32_t>((rr * D + cc * 8) * 4);  // bytes, in a pass
+  const uint32_t lane_off = static_cast<uint32_t>(rr * D * 4 + cc * 16);  // bytes, in a pass
 
   const int64_t per_req = static_cast<int64_t>(a.L) * a.HV;
   const int64_t items = static_cast<int64_t>(a.B) * per_req;
@@ -165,12 +166,18 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
     const uint16_t* kwin = a.rawk + ((static_cast<int64_t>(l) * a.slots + s) * a.H + kh) * a.T * D;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
-      if (t < n) kraw[t] = load_chunk<kBF16>(reinterpret_cast<const char*>(kwin + t * D + cc * 8));
-      else kraw[t] = Chunk<kBF16>{};
+      if (t < n) {
+        // the lane's key columns match its state columns: 4*cc.. and 64 + 4*cc..
+        const u32x2 lo = ld<false, u32x2>(reinterpret_cast<const char*>(kwin + t * D + cc * 4));
+        const u32x2 hi = ld<false, u32x2>(reinterpret_cast<const char*>(kwin + t * D + 64 + cc * 4));
+        kraw[t].w[0] = lo.x; kraw[t].w[1] = lo.y; kraw[t].w[2] = hi.x; kraw[t].w[3] = hi.y;
+      } else {
+        kraw[t] = Chunk<kBF16>{};
+      }
     }
     Chunk<kF32> buf[PD];
 #pragma unroll
-    for (int p = 0; p < PD; ++p) buf[p] = load_chunk<kF32, NTL>(at(tile + p * PS, lane_off));
+    for (int p = 0; p < PD; ++p) buf[p] = load_split_f32<NTL>(at(tile + p * PS, lane_off));
 
     const float alpha_l = expf(g_l);
     wave_lds_fence();
@@ -214,7 +221,7 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
       for (int q = 0; q < PD; ++q) {
         const int p = p0 + q;
         const Chunk<kF32> cur = buf[q];
-        if (p + PD < NPASS) buf[q] = load_chunk<kF32, NTL>(at(tile + (p + PD) * PS, lane_off));
+        if (p + PD < NPASS) buf[q] = load_split_f32<NTL>(at(tile + (p + PD) * PS, lane_off));
         const int r = rr + p * RPP;
         float S[8];
         decode_chunk<kF32>(cur, S);
@@ -244,14 +251,14 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
               Chunk<kF32> o;
 #pragma unroll
               for (int c = 0; c < 8; ++c) o.w[c] = __float_as_uint(S[c]);
-              store_chunk<kF32, NTS>(at(ttile + p * PS, lane_off), o);
+              store_split_f32<NTS>(at(ttile + p * PS, lane_off), o);
             }
           }
         }
         Chunk<kF32> o;
 #pragma unroll
         for (int c = 0; c < 8; ++c) o.w[c] = __float_as_uint(S[c]);
-        store_chunk<kF32, NTS>(at(otile + p * PS, lane_off), o);
+        store_split_f32<NTS>(at(otile + p * PS, lane_off), o);
       }
     }
   }
