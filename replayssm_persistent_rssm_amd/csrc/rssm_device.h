@@ -62,6 +62,16 @@ __device__ __forceinline__ T gload(const T* p) {
   return *(const RSSM_GLOBAL T*)(p);
 }
 
+// Read of a wave-uniform address holding data the kernel never writes, through
+// the scalar data cache (a constant-address-space load).  Its completion is
+// tracked by the scalar/LDS wait counter, so using the value does not wait
+// for the vector loads in flight (a vector load would: their counter retires
+// in order).
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 template <typename T>
 __device__ __forceinline__ void gstore(T* p, T v) {
   *(RSSM_GLOBAL T*)(p) = v;

@@ -514,8 +514,16 @@ rssm_status rssm_ssu_decode(const rssm_ssu_decode_desc* d, const rssm_ssu_decode
   if (fn == nullptr) return fail(RSSM_ERR_UNSUPPORTED, "no decode-step instance for these dtypes and tokens");
   int grid = d->max_workgroups;
   if (grid == 0) {
-    rssm_status st = grid_for(fn, &grid);
+    // One (request, head) item per wavefront, up to 16 times the resident
+    // capacity: measured on MI355X (ssu_large), a grid that streams items in
+    // launch order ran 13% faster than the persistent one (0.222 against
+    // 0.255 ms): the tiles in flight at any moment then lie close together.
+    int resident = 0;
+    rssm_status st = grid_for(fn, &resident);
     if (st != RSSM_OK) return st;
+    const int64_t items = static_cast<int64_t>(d->batch) * d->num_heads;
+    const int64_t want = (items + rssm::kWaves - 1) / rssm::kWaves;
+    grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(16) * resident)));
   }
   rssm::SsuArgs args;
   args.state = static_cast<const char*>(t->state);

@@ -24,15 +24,24 @@
 //  * lane j < n + T holds token j's dt and decay; one suffix-product scan per
 //    new token gives Dec and the weights;
 //  * per (request, group), kept across the heads of the group: C_t for the
-//    lane's 8 columns in registers, and B_j . C_t for every (j, t) in LDS
-//    (16 lanes per dot product, a 16-lane DPP sum);
-//  * with lane = state row, the ring terms and the skip are summed and the
-//    new tokens' x and dt are appended to the ring (B once per group, by the
-//    wavefront that holds the group's first head);
-//  * the checkpoint tile streams through registers, 16 lanes per row and 8
-//    columns per lane, two passes of 4 rows in flight; each row is dotted
-//    with every C_t, the sums pass through LDS to lane = row, and the outputs
-//    are finished and gated.
+//    lane's columns in registers, and B_j . C_t for every (j, t) in LDS (one
+//    lane group per dot product, a DPP sum);
+//  * the checkpoint tile streams through registers, two passes of rows in
+//    flight; each row is dotted with every C_t and the sums pass through LDS
+//    to lane = row;
+//  * with lane = state row, the ring terms and the skip are added and the
+//    outputs gated; the new tokens' x and dt are appended to the ring, and B
+//    once per group, from the group's registers, by the wavefront that holds
+//    the group's first head.
+// The library's default grid gives each wavefront about one item (up to 16
+// times the resident capacity), so the tiles in flight lie close together in
+// memory, which streamed 13% faster than a persistent grid on MI355X.  When a
+// wavefront does get several items (a capped grid, very large batches) they
+// are software-pipelined: before item i streams its tile, item i+1's small
+// inputs (its ring x rows, new x and z rows) are requested straight into the
+// other of two LDS buffers and its dt into a register, and the last passes
+// of i's stream load the first passes of i+1's tile; the scan, ring terms
+// and outputs of i then run while those loads are in flight.
 // The ring entries written are not the pending entries read (n + T <= R), so
 // wavefronts of one request never race.  Instances cover up to TMAX new
 // tokens; for T < TMAX the unused token slots repeat token 0 and their
@@ -69,8 +78,6 @@ constexpr int kSsuDim = 64;
 constexpr int kSsuDstate = 128;
 constexpr int kSsuMaxTokens = 16;   // pending + new tokens one call replays
 
-// Register budget: C costs 8 * TMAX registers per lane.
-template <int TMAX> constexpr int kSsuWavesPerSimd = (TMAX > 4) ? 3 : 4;
 
 // One element of a row in input storage, widened to fp32.
 template <int IT>
@@ -129,6 +136,11 @@ struct SsuRow {
   static constexpr bool kSplit = Fmt<ST>::bytes == 4; // fp32 state: two 4-column halves
   static constexpr int kHalfBytes = 64 * Fmt<ST>::bytes;
 };
+
+// Register budget (resident wavefronts per SIMD): C costs 8 * TMAX registers
+// per lane; the fp32-widened layouts also carry wider row pieces.
+template <int ST, int IT, int TMAX>
+constexpr int kSsuWavesPerSimd = SsuRow<ST, IT>::kPacked ? ((TMAX > 4) ? 3 : 4) : ((TMAX > 4) ? 2 : 3);
 
 // The lane's state chunks of one row; p = row start + cc * 16 bytes.
 template <int ST, int IT, bool NT>
@@ -223,6 +235,36 @@ struct LaneVec {
       for (int i = 0; i < 8; ++i) w[i] = __float_as_uint(f[i]);
     }
   }
+
+  // Write the lane's columns back in the input format (exact: the values
+  // came from that format).
+  __device__ __forceinline__ void store(char* row, int cc) const {
+    constexpr int IB = Fmt<IT>::bytes;
+    if constexpr (Row::kPacked) {
+      st<false>(row + cc * 8 * IB, u32x4{w[0], w[1], w[2], w[3]});
+      st<false>(row + (64 + cc * 8) * IB, u32x4{w[4], w[5], w[6], w[7]});
+    } else {
+      const int c0 = Row::kSplit ? cc * 4 : cc * 8;
+      const int c1 = Row::kSplit ? 64 + cc * 4 : cc * 8 + 4;
+      store4(row + c0 * IB, w);
+      store4(row + c1 * IB, w + 4);
+    }
+  }
+
+ private:
+  __device__ __forceinline__ static void store4(char* p, const uint32_t* f) {
+    if constexpr (IT == kF32) {
+      st<false>(p, u32x4{f[0], f[1], f[2], f[3]});
+    } else {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (IT == kBF16) h[i] = f[i] >> 16;
+        else h[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(__uint_as_float(f[i])));
+      }
+      st<false>(p, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+    }
+  }
 };
 
 // Lane partial of (state row) . C: the lane's state chunks against its columns of C.
@@ -257,8 +299,37 @@ __device__ __forceinline__ float lane_dot_vv(const LaneVec<ST, IT>& x, const Lan
   return v;
 }
 
+// Value of lane + N within the lane's 16-lane DPP row, or 1 where lane + N
+// leaves the row (row_shl with the old value kept, bound_ctrl off).
+template <int N>
+__device__ __forceinline__ float shl_row_or_one(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v), 0x100 + N, 0xF, 0xF,
+                                                    false));
+}
+
+// Request metadata as the kernel uses it (uniform), with the fault guards of
+// the contract: skip slots outside [0, num_slots) and the pad slot, reduce
+// ring_start modulo R, clamp num_buffered to [0, min(16, R) - T].
+struct SsuReq {
+  int b, s, n, r0;
+  bool live;
+  int ent;   // per lane: ring entry of token `lane` (lanes 0..15), (r0 + lane) mod R
+};
+
+__device__ __forceinline__ SsuReq ssu_req(const SsuArgs& a, int b, int s_raw, int r_raw, int n_raw) {
+  SsuReq q;
+  q.b = b;
+  q.s = uniform(s_raw);
+  q.live = q.s != a.pad && q.s >= 0 && q.s < a.num_slots;
+  q.n = min(max(uniform(n_raw), 0), min(kSsuMaxTokens, a.R) - a.T);
+  int r0 = uniform(r_raw) % a.R;
+  q.r0 = r0 < 0 ? r0 + a.R : r0;
+  q.ent = (q.r0 + min(static_cast<int>(threadIdx.x & 63), kSsuMaxTokens - 1)) % a.R;
+  return q;
+}
+
 template <int ST, int IT, int TMAX, int PD = 2>
-__global__ void __launch_bounds__(kBlock, kSsuWavesPerSimd<TMAX>) ssu_decode_kernel(const SsuArgs a) {
+__global__ void __launch_bounds__(kBlock, (kSsuWavesPerSimd<ST, IT, TMAX>)) ssu_decode_kernel(const SsuArgs a) {
   using Row = SsuRow<ST, IT>;
   using CVec = LaneVec<ST, IT>;
   constexpr int DIM = kSsuDim, DS = kSsuDstate;
@@ -273,6 +344,12 @@ __global__ void __launch_bounds__(kBlock, kSsuWavesPerSimd<TMAX>) ssu_decode_ker
   constexpr int MM = kSsuMaxTokens;
   constexpr int NRING = MM - 1;            // pending entries: n <= 16 - T <= 15
   constexpr int DSTRIDE = DIM + RPP;       // row sums per token in LDS, padded against bank conflicts
+  // rows of 64 input elements move as 16-byte pieces, one per lane
+  constexpr int ROWB = DIM * IB;           // bytes per x row
+  constexpr int LPX = ROWB / 16;           // lanes per x row
+  constexpr int XPI = 64 / LPX;            // x rows per load instruction
+  constexpr int NXI = MM / XPI;            // instructions for 16 ring rows
+  constexpr int NZI = (2 * TMAX + XPI - 1) / XPI;   // instructions for T new-x rows and T z rows
   static_assert(TMAX >= 1 && TMAX <= 8, "TMAX");
   static_assert(NPASS % PD == 0, "passes");
   static_assert(TMAX <= TPR, "one lane of each row stores each token's row sum");
@@ -280,6 +357,8 @@ __global__ void __launch_bounds__(kBlock, kSsuWavesPerSimd<TMAX>) ssu_decode_ker
   __shared__ float lds_beta[kWaves][MM * TMAX];     // B_j . C_t at [j][t]
   __shared__ float lds_c[kWaves][MM * TMAX];        // w_j^(n+t+1) (B_j . C_t) at [j][t]
   __shared__ float lds_dot[kWaves][TMAX * DSTRIDE]; // S_0[r,:] . C_t at [t][r]
+  __shared__ u32x4 lds_x[kWaves][2][NXI * 64];      // ring x rows j = 0..15, ROWB bytes each (two items)
+  __shared__ u32x4 lds_xz[kWaves][2][NZI * 64];     // x_new rows t < T, then z rows (two items)
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
@@ -293,82 +372,114 @@ __global__ void __launch_bounds__(kBlock, kSsuWavesPerSimd<TMAX>) ssu_decode_ker
   float* beta = lds_beta[wave];
   float* cw = lds_c[wave];
   float* dots = lds_dot[wave];
+  const int xrow_l = lane / LPX;                    // row of this lane's 16-byte piece
+  const uint32_t xpiece = static_cast<uint32_t>((lane % LPX) * 16);
 
+  // ---- the wavefront's items, in order -------------------------------------
   const int64_t items = static_cast<int64_t>(a.B) * H;
   const int64_t tw = static_cast<int64_t>(gridDim.x) * kWaves;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   constexpr int64_t kC = 16;
   const int64_t csz = min(kC, (items + tw - 1) / tw);
-  int64_t chunk = gw;
-  int64_t it = chunk * csz, end = min(items, it + csz);
+  int64_t chunk = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  int64_t nxt = chunk * csz;                         // next item not yet taken (-1: none)
+  int64_t cend = min(items, nxt + csz);
+  if (nxt >= items) nxt = -1;
+  auto advance = [&]() {
+    if (nxt < 0) return;
+    if (++nxt >= cend) {
+      chunk += tw;
+      nxt = chunk * csz;
+      if (nxt >= items) {
+        nxt = -1;
+        return;
+      }
+      cend = min(items, nxt + csz);
+    }
+  };
 
-  int cur_b = -1, cur_g = -1, s = 0, n = 0;
-  int ent_l = 0;   // ring entry of token `lane` of the current request
-  bool live = false;
+  // ---- loads in flight for the upcoming item --------------------------------
+  float p_dt = 0.0f;           // token `lane`'s dt before bias / softplus (pending: as stored)
+  Chunk<ST> buf[PD][NCH];      // the first passes of its tile
+  // its ring x rows and its new x and z rows go straight to LDS (direct
+  // global-to-LDS loads: lane L's 16 bytes land at the region's base + 16 L)
+  auto to_lds = [&](const char* src, u32x4* region) {
+    __builtin_amdgcn_global_load_lds((const RSSM_GLOBAL void*)(src), (__attribute__((address_space(3))) void*)(region),
+                                     16, 0, 0);
+  };
+  auto issue_small = [&](const SsuReq& q, int h, int sb) {
+    const int tnew = min(max(lane - q.n, 0), T - 1);
+    p_dt = gload(lane < q.n ? a.dt_ring + static_cast<int64_t>(q.s) * a.dt_stride + static_cast<int64_t>(q.ent) * H + h
+                            : a.dt_new + (q.b * rowsT + tnew) * H + h);
+    const char* xslot = a.x_ring + (static_cast<int64_t>(q.s) * a.x_stride + h * DIM) * IB;
+#pragma unroll
+    for (int k = 0; k < NXI; ++k) {
+      const int j = k * XPI + xrow_l;
+      const int e = __shfl(q.ent, min(j, MM - 1));   // every lane takes part in the exchange
+      if (k * XPI < q.n && j < q.n) to_lds(xslot + static_cast<int64_t>(e) * H * ROWB + xpiece, &lds_x[wave][sb][k * 64]);
+    }
+#pragma unroll
+    for (int k = 0; k < NZI; ++k) {
+      const int rrow = k * XPI + xrow_l;
+      if (rrow < 2 * T) {
+        const bool isz = rrow >= T;
+        const int t = isz ? rrow - T : rrow;
+        const char* base = isz ? a.z : a.x_new;
+        to_lds(base + (((q.b * rowsT + t) * H + h) * DIM) * IB + xpiece, &lds_xz[wave][sb][k * 64]);
+      }
+    }
+  };
+  auto tile_of = [&](const SsuReq& q, int h) {
+    return a.state + (static_cast<int64_t>(q.s) * a.state_stride + h * kTile) * SB;
+  };
+
+  SsuReq cur{-1, 0, 0, 0, false, 0}, nq{-1, 0, 0, 0, false, 0};
+  int cur_g = -1, cur_gb = -1;
+  int sb = 0;                  // LDS row-piece buffer of the upcoming item
+  bool have = false;           // the loads above belong to item `nxt`
   CVec Cv[TMAX];
   while (true) {
-    if (it >= end) {
-      chunk += tw;
-      it = chunk * csz;
-      if (it >= items) break;
-      end = min(items, it + csz);
+    if (!have) {
+      // cold start: the next live item, its request's metadata read here
+      while (nxt >= 0) {
+        const int b = static_cast<int>(nxt / H);
+        if (b != nq.b) nq = ssu_req(a, b, sload(a.slots + b), sload(a.ring_start + b), sload(a.num_buffered + b));
+        if (nq.live) break;
+        advance();
+      }
+      if (nxt < 0) break;
+      const int h0 = static_cast<int>(nxt - static_cast<int64_t>(nq.b) * H);
+      const char* t0 = tile_of(nq, h0);
+#pragma unroll
+      for (int p = 0; p < PD; ++p) load_lane_state<ST, IT, true>(at(t0 + p * PS, lane_off), buf[p]);
+      issue_small(nq, h0, sb);
     }
-    const int b = uniform(static_cast<int>(it / H));
-    const int h = uniform(static_cast<int>(it - static_cast<int64_t>(b) * H));
-    ++it;
-    if (b != cur_b) {
-      cur_b = b;
-      cur_g = -1;
-      const int s_raw = gload(a.slots + b), r_raw = gload(a.ring_start + b), n_raw = gload(a.num_buffered + b);
-      s = uniform(s_raw);
-      // guards against faults; the contract keeps every value in range
-      live = s != a.pad && s >= 0 && s < a.num_slots;
-      n = min(max(uniform(n_raw), 0), min(MM, a.R) - T);
-      int r0 = uniform(r_raw) % a.R;
-      if (r0 < 0) r0 += a.R;
-      ent_l = (r0 + lane) % a.R;
-    }
-    if (!live) continue;
+    // ---- take the item ------------------------------------------------------
+    cur = nq;
+    const int h = uniform(static_cast<int>(nxt - static_cast<int64_t>(cur.b) * H));
+    const int b = cur.b, s = cur.s, n = cur.n;
     const int g = h / a.hpg;
     const int m = n + T;
-
-    // ---- requests of the item, issued together ----------------------------
-    const char* tile = a.state + (static_cast<int64_t>(s) * a.state_stride + h * kTile) * SB;
-    Chunk<ST> buf[PD][NCH];
-#pragma unroll
-    for (int p = 0; p < PD; ++p) load_lane_state<ST, IT, true>(at(tile + p * PS, lane_off), buf[p]);
-    // token `lane`: dt from the ring (pending) or from the step's inputs (new)
-    const bool pend_l = lane < n;
-    const int tnew_l = min(max(lane - n, 0), T - 1);
-    const float* dsrc = pend_l ? a.dt_ring + static_cast<int64_t>(s) * a.dt_stride + static_cast<int64_t>(ent_l) * H + h
-                               : a.dt_new + (b * rowsT + tnew_l) * H + h;
-    const float dt_raw = gload(dsrc);
-    const float A_h = gload(a.A + h);
-    const float bias_h = gload(a.dt_bias + h);
-    const float D_h = gload(a.D + h);
-    // row `lane` of x_j: pending entries from the ring (32-bit offsets from
-    // the slot's ring base), new tokens raw; z for the gate
-    char* xslot = a.x_ring + static_cast<int64_t>(s) * a.x_stride * IB;
-    const uint32_t xrow = static_cast<uint32_t>((h * DIM + lane) * IB);
-    const uint32_t xent = static_cast<uint32_t>(H * DIM * IB);
-    uint32_t xraw[NRING];
-#pragma unroll
-    for (int j = 0; j < NRING; ++j) {
-      const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readlane(ent_l, j < n ? j : 0));
-      xraw[j] = load_elem<IT>(at(xslot, e * xent + xrow));
+    const char* tile = tile_of(cur, h);
+    const int cb = sb;         // this item's row pieces
+    sb ^= 1;
+    const float dt_raw = p_dt;
+    advance();
+    // the following item's request metadata
+    const int b2 = nxt >= 0 ? static_cast<int>(nxt / H) : -1;
+    int s2_raw = 0, r2_raw = 0, n2_raw = 0;
+    if (b2 >= 0 && b2 != b) {
+      s2_raw = sload(a.slots + b2);
+      r2_raw = sload(a.ring_start + b2);
+      n2_raw = sload(a.num_buffered + b2);
     }
-    uint32_t xn[TMAX], zr[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      const int tt = t < T ? t : 0;
-      const int64_t yi = ((b * rowsT + tt) * H + h) * DIM + lane;
-      xn[t] = load_elem<IT>(a.x_new + yi * IB);
-      zr[t] = load_elem<IT>(a.z + yi * IB);
-    }
+    const float A_h = sload(a.A + h);
+    const float bias_h = sload(a.dt_bias + h);
+    const float D_h = sload(a.D + h);
 
     // ---- per (request, group): C_t in registers, B_j . C_t in LDS ----------
-    if (g != cur_g) {
+    if (g != cur_g || b != cur_gb) {
       cur_g = g;
+      cur_gb = b;
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) {
         const int tt = t < T ? t : 0;
@@ -378,14 +489,18 @@ __global__ void __launch_bounds__(kBlock, kSsuWavesPerSimd<TMAX>) ssu_decode_ker
 #pragma unroll
       for (int q = 0; q < MM / RPP; ++q) {
         const int j = rr + RPP * q;   // token of this lane group
-        const int ej = __shfl(ent_l, j);
+        const int ej = __shfl(cur.ent, j);
         const int tj = min(max(j - n, 0), T - 1);
         const char* src = (j < n) ? a.B_ring + (static_cast<int64_t>(s) * a.B_stride +
                                                 (static_cast<int64_t>(ej) * G + g) * DS) * IB
                                   : a.B_new + (((b * rowsT + tj) * G + g) * DS) * IB;
         bc[q].load(src, cc);
+        // the group's first head appends the new tokens' B rows from these registers
+        if (h % a.hpg == 0 && j >= n && j < m)
+          bc[q].store(a.B_ring + (static_cast<int64_t>(s) * a.B_stride + (static_cast<int64_t>(ej) * G + g) * DS) * IB,
+                      cc);
       }
-      wave_lds_fence();   // the previous group's readers are done with beta
+      wave_lds_fence();   // the previous item's readers of beta are done
 #pragma unroll
       for (int q = 0; q < MM / RPP; ++q) {
         const int j = rr + RPP * q;
@@ -399,7 +514,61 @@ __global__ void __launch_bounds__(kBlock, kSsuWavesPerSimd<TMAX>) ssu_decode_ker
       }
     }
 
-    // ---- decays and weights: one suffix-product scan per new token -------
+    // ---- the following item: metadata, small loads (into the other row-piece
+    // buffer, which no one reads now), first passes from the stream's tail ---
+    have = false;
+    if (nxt >= 0) {
+      if (b2 != b) nq = ssu_req(a, b2, s2_raw, r2_raw, n2_raw);
+      if (nq.live) have = true;
+    }
+    const int h2 = have ? uniform(static_cast<int>(nxt - static_cast<int64_t>(nq.b) * H)) : 0;
+    const char* ntile = tile_of(nq, h2);
+    if (have) issue_small(nq, h2, sb);
+
+    // ---- stream the checkpoint tile: S_0[r,:] . C_t for every row and t ---
+    // (fully unrolled: straight-line code lets each pass wait only for its own
+    // loads, with the next passes still in flight)
+    wave_lds_fence();   // the previous item's readers of the row sums are done
+#pragma unroll
+    for (int p0 = 0; p0 < NPASS; p0 += PD) {
+#pragma unroll
+      for (int q = 0; q < PD; ++q) {
+        const int p = p0 + q;
+        Chunk<ST> cur_c[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) cur_c[k] = buf[q][k];
+        if (p + PD < NPASS) load_lane_state<ST, IT, true>(at(tile + (p + PD) * PS, lane_off), buf[q]);
+        else if (have) load_lane_state<ST, IT, true>(at(ntile + (p + PD - NPASS) * PS, lane_off), buf[q]);
+        float sel = 0.0f;
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+          const float v = row_sum<TPR>(lane_dot<ST, IT>(cur_c, Cv[t]));
+          if (cc == t) sel = v;
+        }
+        if (cc < TMAX) dots[cc * DSTRIDE + rr + p * RPP] = sel;
+      }
+    }
+
+    // ---- after the stream (the next tile's first passes are in flight) ------
+    // this item's row pieces: append the new x rows to the ring
+    const char* xl = reinterpret_cast<const char*>(lds_x[wave][cb]);
+    const char* xzl = reinterpret_cast<const char*>(lds_xz[wave][cb]);
+#pragma unroll
+    for (int k = 0; k < NZI; ++k) {
+      const int t = k * XPI + xrow_l;
+      const int e = __shfl(cur.ent, min(n + t, MM - 1));   // every lane takes part in the exchange
+      if (t < T) {
+        st<false>(a.x_ring + (static_cast<int64_t>(s) * a.x_stride + (static_cast<int64_t>(e) * H + h) * DIM) * IB +
+                      xpiece,
+                  lds_xz[wave][cb][k * 64 + lane]);
+      }
+    }
+    auto xelem = [&](const char* base, int row) -> float {
+      if constexpr (IB == 4) return *reinterpret_cast<const float*>(base + row * ROWB + lane * 4);
+      else return input_to_float<IT>(*reinterpret_cast<const uint16_t*>(base + row * ROWB + lane * 2));
+    };
+
+    // decays and weights: one suffix-product scan per new token
     float dt_l = dt_raw;
     if (lane >= n && lane < m) dt_l = new_token_dt(dt_raw, a.has_bias ? bias_h : 0.0f, a.dt_softplus);
     if (lane >= m) dt_l = 0.0f;
@@ -409,94 +578,59 @@ __global__ void __launch_bounds__(kBlock, kSsuWavesPerSimd<TMAX>) ssu_decode_ker
     for (int t = 0; t < TMAX; ++t) {
       const int mt = n + t + 1;
       float P = (lane < mt) ? a_l : 1.0f;   // after the scan: prod over lanes lane .. min(mt, 16)-1
-#pragma unroll
-      for (int off = 1; off < MM; off <<= 1) {
-        const float o = __shfl_down(P, off);
-        if (lane + off < MM) P *= o;
-      }
-      float Pn = __shfl_down(P, 1);
+      // Hillis-Steele suffix products inside the first DPP row (lanes 0..15;
+      // the other rows hold ones): row_shl brings lane j + off, and lanes whose
+      // source leaves the row keep the old value 1
+      P *= shl_row_or_one<1>(P);
+      P *= shl_row_or_one<2>(P);
+      P *= shl_row_or_one<4>(P);
+      P *= shl_row_or_one<8>(P);
+      float Pn = shl_row_or_one<1>(P);
       if (lane + 1 >= mt) Pn = 1.0f;
       dec[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P), 0));
       w[t] = (lane < mt) ? dt_l * Pn : 0.0f;
     }
-    wave_lds_fence();   // beta written; the previous item's readers of cw are done
+    wave_lds_fence();   // beta and the row sums written; the previous item's readers of cw are done
     if (lane < MM) {
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) cw[lane * TMAX + t] = w[t] * beta[lane * TMAX + t];
     }
     wave_lds_fence();
 
-    // ---- the ring terms and the skip (lane = state row), then the append --
+    // the ring terms, the skip and the outputs (lane = state row); dt append
     float yp[TMAX];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) yp[t] = 0.0f;
+    for (int t = 0; t < TMAX; ++t) yp[t] = dec[t] * dots[t * DSTRIDE + lane];
 #pragma unroll
     for (int j = 0; j < NRING; ++j) {
-      const float x = (j < n) ? input_to_float<IT>(xraw[j]) : 0.0f;
+      if (j < n) {
+        const float x = xelem(xl, j);
 #pragma unroll
-      for (int t = 0; t < TMAX; ++t) yp[t] = fmaf(cw[j * TMAX + t], x, yp[t]);
+        for (int t = 0; t < TMAX; ++t) yp[t] = fmaf(cw[j * TMAX + t], x, yp[t]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < TMAX; ++u) {
       if (u < T) {
-        const float x = input_to_float<IT>(xn[u]);
+        const float x = xelem(xzl, u);
         const float* cu = cw + (n + u) * TMAX;   // zero for outputs t < u
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) yp[t] = fmaf(cu[t], x, yp[t]);
+        if (a.has_D) yp[u] = fmaf(D_h, x, yp[u]);
       }
-    }
-    if (a.has_D) {
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) yp[t] = fmaf(D_h, input_to_float<IT>(xn[t]), yp[t]);
     }
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        const int e = __builtin_amdgcn_readlane(ent_l, n + t);
-        store_elem<IT>(at(xslot, static_cast<uint32_t>(e) * xent + xrow), xn[t]);
-        if (lane == n + t)
-          gstore(a.dt_ring + static_cast<int64_t>(s) * a.dt_stride + static_cast<int64_t>(e) * H + h, dt_l);
-        if (h % a.hpg == 0) {
-          const char* bs = a.B_new + (((b * rowsT + t) * G + g) * DS) * IB;
-          char* bd = a.B_ring + (static_cast<int64_t>(s) * a.B_stride + (static_cast<int64_t>(e) * G + g) * DS) * IB;
-#pragma unroll
-          for (int q = 0; q < DS / 64; ++q)
-            store_elem<IT>(bd + (lane + 64 * q) * IB, load_elem<IT>(bs + (lane + 64 * q) * IB));
-        }
-      }
-    }
-
-    // ---- stream the checkpoint tile: S_0[r,:] . C_t for every row and t ---
-#pragma unroll 1
-    for (int p0 = 0; p0 < NPASS; p0 += PD) {
-#pragma unroll
-      for (int q = 0; q < PD; ++q) {
-        const int p = p0 + q;
-        Chunk<ST> cur[NCH];
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) cur[k] = buf[q][k];
-        if (p + PD < NPASS) load_lane_state<ST, IT, true>(at(tile + (p + PD) * PS, lane_off), buf[q]);
-        float sel = 0.0f;
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-          const float v = row_sum<TPR>(lane_dot<ST, IT>(cur, Cv[t]));
-          if (cc == t) sel = v;
-        }
-        if (cc < TMAX) dots[cc * DSTRIDE + rr + p * RPP] = sel;
-      }
-    }
-    wave_lds_fence();
-
-    // ---- outputs ------------------------------------------------------------
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T) {
-        float y = fmaf(dec[t], dots[t * DSTRIDE + lane], yp[t]);
+        float y = yp[t];
         if (a.has_z) {
-          const float zv = input_to_float<IT>(zr[t]);
-          y *= zv / (1.0f + expf(-zv));
+          const float zv = xelem(xzl, T + t);
+          y *= zv * __builtin_amdgcn_rcpf(1.0f + expf(-zv));   // silu, reciprocal within 1 ulp
         }
         gstore(a.y + ((b * rowsT + t) * H + h) * DIM + lane, y);
+        const int e = __builtin_amdgcn_readlane(cur.ent, n + t);
+        if (lane == n + t)
+          gstore(a.dt_ring + static_cast<int64_t>(s) * a.dt_stride + static_cast<int64_t>(e) * H + h, dt_l);
       }
     }
   }
