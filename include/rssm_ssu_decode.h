@@ -55,7 +55,9 @@ extern "C" {
  *   state_dtype        RSSM_F32 | RSSM_BF16 | RSSM_F16
  *   input_dtype        x, B, C, z and the x and B rings: RSSM_F32 | RSSM_BF16 | RSSM_F16
  *   dt_softplus        1: dt = softplus(dt_raw + bias); 0: dt = dt_raw + bias
- *   max_workgroups     0: occupancy-sized persistent grid; > 0: exactly this many
+ *   max_workgroups     0: about one (request, head) item per wavefront, at most
+ *                      16 times the resident capacity; > 0: exactly this many
+ *                      workgroups (results do not depend on it)
  *   *_slot_stride      distance between consecutive slots of each pool, in
  *                      ELEMENTS; at least the dense per-slot size below */
 typedef struct {

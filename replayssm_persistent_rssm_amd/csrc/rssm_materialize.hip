@@ -241,6 +241,19 @@ rssm_status grid_for(const void* fn, int* grid_out) {
   return RSSM_OK;
 }
 
+// Default grid of the materialize kernels: four times the resident capacity.
+// The work loop is persistent either way; measured on MI355X in one process,
+// the oversubscribed grid ran 5-6% faster on the int8 and e4m3 workloads and
+// within 0.5% on bf16, and kept the empty call at 3.6-4.7 us (eight times
+// the capacity gained a little more but pushed the empty call past 5 us).
+rssm_status materialize_grid(const void* fn, int* grid_out) {
+  int resident = 0;
+  rssm_status st = grid_for(fn, &resident);
+  if (st != RSSM_OK) return st;
+  *grid_out = 4 * resident;
+  return RSSM_OK;
+}
+
 // The last descriptor validated on this thread, with its instance and grid
 // on that device: a serving loop calls with the same scalars every step.
 struct LaunchCache {
@@ -290,7 +303,7 @@ rssm_status launch(const rssm_materialize_desc* desc, const rssm_materialize_tab
   } else {
     grid = desc->max_workgroups;
     if (grid == 0) {
-      st = grid_for(k->fn, &grid);
+      st = materialize_grid(k->fn, &grid);
       if (st != RSSM_OK) return st;
     }
     g_last.desc = *desc;
@@ -355,7 +368,7 @@ rssm_status rssm_materialize_launch_config(const rssm_materialize_desc* desc, in
   if (desc->max_workgroups > 0) {
     g = desc->max_workgroups;
   } else {
-    st = grid_for(k->fn, &g);
+    st = materialize_grid(k->fn, &g);
     if (st != RSSM_OK) return st;
   }
   *grid = g;
