@@ -241,16 +241,17 @@ rssm_status grid_for(const void* fn, int* grid_out) {
   return RSSM_OK;
 }
 
-// Default grid of the materialize kernels: four times the resident capacity.
-// The work loop is persistent either way; measured on MI355X in one process,
-// the oversubscribed grid ran 5-6% faster on the int8 and e4m3 workloads and
-// within 0.5% on bf16, and kept the empty call at 3.6-4.7 us (eight times
-// the capacity gained a little more but pushed the empty call past 5 us).
-rssm_status materialize_grid(const void* fn, int* grid_out) {
+// Default grid of the materialize kernels (the work loop is persistent either
+// way).  One-byte state: four times the resident capacity, which ran 5-6%
+// faster than one workgroup per resident slot on the int8 and e4m3 workloads
+// on MI355X (their requests differ more in cost).  Other state: the resident
+// capacity; four times it was within 0.5% on bf16 but raised the empty call's
+// kernel time from 2.5 to 3.5 us.
+rssm_status materialize_grid(const rssm_materialize_desc* d, const void* fn, int* grid_out) {
   int resident = 0;
   rssm_status st = grid_for(fn, &resident);
   if (st != RSSM_OK) return st;
-  *grid_out = 4 * resident;
+  *grid_out = one_byte(d->state_dtype) ? 4 * resident : resident;
   return RSSM_OK;
 }
 
@@ -303,7 +304,7 @@ rssm_status launch(const rssm_materialize_desc* desc, const rssm_materialize_tab
   } else {
     grid = desc->max_workgroups;
     if (grid == 0) {
-      st = materialize_grid(k->fn, &grid);
+      st = materialize_grid(desc, k->fn, &grid);
       if (st != RSSM_OK) return st;
     }
     g_last.desc = *desc;
@@ -368,7 +369,7 @@ rssm_status rssm_materialize_launch_config(const rssm_materialize_desc* desc, in
   if (desc->max_workgroups > 0) {
     g = desc->max_workgroups;
   } else {
-    st = materialize_grid(k->fn, &g);
+    st = materialize_grid(desc, k->fn, &g);
     if (st != RSSM_OK) return st;
   }
   *grid = g;
