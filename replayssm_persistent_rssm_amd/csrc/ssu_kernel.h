@@ -87,18 +87,6 @@ __device__ __forceinline__ float input_to_float(uint32_t raw) {
   else return f16_bits_to_float(raw);
 }
 
-template <int IT>
-__device__ __forceinline__ uint32_t load_elem(const char* p) {
-  if constexpr (Fmt<IT>::bytes == 4) return gload(reinterpret_cast<const uint32_t*>(p));
-  else return gload(reinterpret_cast<const uint16_t*>(p));
-}
-
-template <int IT>
-__device__ __forceinline__ void store_elem(char* p, uint32_t v) {
-  if constexpr (Fmt<IT>::bytes == 4) gstore(reinterpret_cast<uint32_t*>(p), v);
-  else gstore(reinterpret_cast<uint16_t*>(p), static_cast<uint16_t>(v));
-}
-
 // dt of a new token, softplus(raw + bias) (or the plain sum), in fp32.  The
 // sum is kept as an unevaluated pair hi + lo (Knuth's TwoSum) so that the
 // softplus sees the exact input: rounding the sum first would cost |v| u
@@ -137,10 +125,13 @@ struct SsuRow {
   static constexpr int kHalfBytes = 64 * Fmt<ST>::bytes;
 };
 
-// Register budget (resident wavefronts per SIMD): C costs 8 * TMAX registers
-// per lane; the fp32-widened layouts also carry wider row pieces.
+// Resident wavefronts per SIMD the registers are budgeted for: C costs
+// 8 * TMAX registers per lane, the fp32-widened layouts more; fp32 inputs
+// double the LDS row buffers (55 KiB per workgroup at TMAX 4), which caps
+// them at 2 anyway.
 template <int ST, int IT, int TMAX>
-constexpr int kSsuWavesPerSimd = SsuRow<ST, IT>::kPacked ? ((TMAX > 4) ? 3 : 4) : ((TMAX > 4) ? 2 : 3);
+constexpr int kSsuWavesPerSimd = SsuRow<ST, IT>::kPacked ? ((TMAX > 4) ? 3 : 4)
+                                 : (Fmt<IT>::bytes == 4 || TMAX > 4) ? 2 : 3;
 
 // The lane's state chunks of one row; p = row start + cc * 16 bytes.
 template <int ST, int IT, bool NT>
