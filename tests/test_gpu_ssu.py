@@ -99,6 +99,8 @@ VARIANTS = [
     dict(state_dtype="bf16", input_dtype="f32"),
     dict(state_dtype="f32", input_dtype="bf16"),
     dict(state_dtype="f16", input_dtype="bf16"),
+    dict(state_dtype="f32", input_dtype="f16"),
+    dict(state_dtype="bf16", input_dtype="f16", T=6),
     dict(T=1),
     dict(T=3, buffered=[13, 0, 7, 12, 1]),
     dict(T=5),
@@ -232,3 +234,65 @@ def test_full_size_sampled(dev):
     assert (err <= TOL * ym).all()
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", [90, 91])
+def test_decode_flush_decode_chain(dev, seed):
+    """The serving loop on the GPU: a decode step appends T tokens, an in-place
+    materialize flushes all n + T buffered tokens into the checkpoint, and a
+    second decode step starts from that checkpoint with an empty ring window.
+    Its outputs equal the oracle's decode step run on the ORIGINAL checkpoint
+    with n + T pending entries (the oracle's own appended ring) and the same
+    second tokens.  fp32 state, so the flush rounds the state once to fp32,
+    which the tolerance's M bound covers."""
+    import copy
+    import torch
+    import oracle
+    import rssm_harness as hx
+    spec = ri.with_(ri.SSU_CONFIGS["ssu_small"], state_dtype="f32", input_dtype="f32", buffered=[3, 0, 8, 5, 1])
+    p1 = ri.make_ssu_problem(spec, seed)
+    p2 = ri.make_ssu_problem(spec, seed + 100)   # the second step's tokens
+    T, R = spec.T, spec.R
+    say("chain seed", seed, "slots", p1.slots.tolist(), "buffered", p1.num_buffered.tolist())
+    # device pools shared by the three calls
+    dp = hx.upload(p1.pools, dev)
+    m = dp.meta
+    live = np.array([int(s) != spec.pad_slot_id for s in p1.slots])
+    t32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if a is not None else None  # noqa: E731
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+
+    def step(p, ring_start, buffered):
+        y = torch.full((spec.B, T, spec.H, spec.dim), float("nan"), dtype=torch.float32, device=dev)
+        d = ri.SsuDeviceProblem(spec=spec, state=dp.state[0], x_ring=dp.x[0], B_ring=dp.Bm[0], dt_ring=dp.dt[0],
+                                A=dp.A[0], D=t32(p.D), dt_bias=t32(p.dt_bias), x_new=t32(p.x_new), B_new=t32(p.B_new),
+                                C_new=t32(p.C_new), dt_new=t32(p.dt_new), z=t32(p.z), y=y, slots=i32(p1.slots),
+                                ring_start=i32(ring_start), num_buffered=i32(buffered), slots_np=p1.slots,
+                                ring_start_np=ring_start, num_buffered_np=buffered)
+        hx.ssu_call(d)
+        return y
+
+    step(p1, p1.ring_start, p1.num_buffered)
+    # flush in place: src = dst = the request's slot, prefix n + T from its ring start
+    m.src[0] = p1.slots
+    m.dst[0] = p1.slots
+    m.ring_start[:] = p1.ring_start
+    m.prefix[:] = p1.num_buffered + T
+    act = np.full(spec.B, -1, np.int32)
+    act[:int(live.sum())] = np.nonzero(live)[0]
+    hx.materialize(dp, hx.tables(dp, dev), active=i32(act))
+    rs2 = ((p1.ring_start + p1.num_buffered + T) % R).astype(np.int32)
+    y2 = step(p2, rs2, np.zeros(spec.B, np.int32)).cpu().numpy()
+    torch.cuda.synchronize()
+
+    # the oracle: the original checkpoint, its own appended ring, n + T pending, the second tokens
+    xr, Br, dtr, _, _, _ = oracle.ssu_decode(p1)
+    q = copy.deepcopy(p2)
+    q.pools = copy.deepcopy(p1.pools)
+    q.pools.x[0], q.pools.Bm[0], q.pools.dt[0] = xr, Br, dtr
+    q.slots, q.ring_start, q.A = p1.slots, p1.ring_start, p1.A
+    q.num_buffered = (p1.num_buffered + T).astype(np.int32)
+    _, _, _, y, ym, _ = oracle.ssu_decode(q)
+    err = np.abs(y2[live].astype(np.float64) - y[live])
+    say("chain: max |gpu-exact|/M", float((err / np.maximum(ym[live], 1e-300)).max()))
+    assert (err <= TOL * ym[live]).all()
+    assert np.isnan(y2[~live]).all()
