@@ -129,6 +129,8 @@ def main():
                     help="workload of the profile modes (the headline line always uses large_bf16)")
     ap.add_argument("--only-gdn", action="store_true",
                     help="profile mode: the gated-delta-rule commit line only")
+    ap.add_argument("--plain-alloc", action="store_true",
+                    help="plain hipMalloc pools (torch's caching allocator) instead of physically contiguous ones")
     ap.add_argument("--only-ssu", action="store_true",
                     help="profile mode: the decode-step line only")
     ap.add_argument("--only-checkpoints", action="store_true",
@@ -163,6 +165,9 @@ def main():
     import rssm_inputs as ri
     import replayssm_persistent_rssm_amd as rp
 
+    if not args.plain_alloc:
+        # the pools physically contiguous (before the process allocates anything)
+        rp.use_contiguous_allocator()
     dev = torch.device("cuda:0")
     if args.only_gdn:
         print(json.dumps({"gdn_commit": gdn_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
@@ -225,7 +230,8 @@ def main():
         "config": {"workload": "large_bf16: L=48, B=256 (256 active), H=256 (8 groups), state 64x128, "
                                "bf16 state/x/B, fp32 dt/A, R=16, max_window=8, k~U[1,8]",
                    "storage": "bf16", "accumulate": "f32", "grid": grid, "block": block, "lds_bytes": lds,
-                   "algorithmic_bytes_per_call": full_bytes},
+                   "algorithmic_bytes_per_call": full_bytes,
+                   "pools": "hipMalloc" if args.plain_alloc else "physically contiguous (rssm_pool.h)"},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(full_bytes),
                      "kernel": "materialize_kernel<bf16,bf16,64x128,kmax8>", "kernel_source_hash": kernel_hash()},

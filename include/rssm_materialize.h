@@ -15,9 +15,10 @@
  * near-empty launch.
  *
  * Nothing here crosses the ABI but plain C types.  Every pointer inside
- * rssm_materialize_tables is DEVICE memory owned by the caller; the library
- * allocates nothing, keeps no reference after the call returns, and reads no
- * device memory on the host (the call never synchronises).  The caller keeps
+ * rssm_materialize_tables is DEVICE memory owned by the caller; the call
+ * allocates nothing, keeps no reference after it returns, and reads no
+ * device memory on the host (it never synchronises).  (rssm_pool.h offers
+ * physically contiguous memory for the pools.)  The caller keeps
  * every buffer alive until the enqueued work has completed on the stream.
  */
 #ifndef RSSM_MATERIALIZE_H

@@ -11,4 +11,5 @@ from ._binding import (  # noqa: F401
     rssm_debug_encode_rows, rssm_last_error, rssm_materialize, rssm_materialize_checkpoints,
     rssm_materialize_launch_config, RSSM_MAX_CHECKPOINTS, stride_table, rssm_gdn_commit,
     gated_delta_rule_replayssm_commit, GdnCommitCall, RssmGdnDesc, RssmGdnTables, rssm_ssu_decode,
-    SsuDecodeCall, RssmSsuDesc, RssmSsuTables, RSSM_SSU_MAX_TOKENS, RSSM_SSU_MAX_REPLAY)
+    SsuDecodeCall, RssmSsuDesc, RssmSsuTables, RSSM_SSU_MAX_TOKENS, RSSM_SSU_MAX_REPLAY, rssm_pool_alloc,
+    rssm_pool_free, use_contiguous_allocator)

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "librssm_materialize.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["rssm_inst_f32.hip", "rssm_inst_bf16.hip", "rssm_inst_f16.hip", "rssm_inst_i8.hip",
-           "rssm_inst_f8.hip", "rssm_inst_gdn.hip", "rssm_inst_ssu.hip", "rssm_materialize.hip"]
+           "rssm_inst_f8.hip", "rssm_inst_gdn.hip", "rssm_inst_ssu.hip", "rssm_pool.hip", "rssm_materialize.hip"]
 ARCH = os.environ.get("RSSM_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -289,3 +289,12 @@ def test_ssu_byte_count():
     want = 3 * H * 4 + H * dim * ds * 2 + 3 * (H * (dim * 2 + 4) + G * ds * 2)
     want += T * (H * (2 * dim * 2 + 4) + 2 * G * ds * 2) + T * H * dim * 4 + T * (H * (dim * 2 + 4) + G * ds * 2)
     assert hx.ssu_bytes(spec, [7, spec.pad_slot_id], [3, 5]) == want
+
+
+def test_pool_alloc_validation(rp):
+    """Host validation of the pool allocator, before any HIP call."""
+    out = ctypes.c_void_p(123)
+    assert rp.lib().rssm_pool_alloc(ctypes.c_uint64(1 << 20), None, None) == 1
+    assert rp.lib().rssm_pool_alloc(ctypes.c_uint64(0), ctypes.byref(out), None) == 1
+    assert out.value is None
+    assert rp.lib().rssm_pool_free(None) == 0
