@@ -328,7 +328,17 @@ def main():
         torch.cuda.synchronize()
         t_graph = timed_calls(g.replay, 10, stream) / 100
         result["empty_launch_us_graph"] = round(t_graph * 1e3, 3)
-        say(f"empty launch: {t_empty * 1e3:.2f} us (stream), {t_graph * 1e3:.2f} us (graph)")
+        # every request listed, every source slot the pad slot: work discovery over all
+        # (request, layer) pairs, nothing written
+        pad_src = torch.full((spec.L, spec.B), spec.pad_slot_id, dtype=torch.int32, device=dev)
+        pad_call = hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "src_slots": pad_src}))
+        for _ in range(20):
+            pad_call()
+        torch.cuda.synchronize()
+        t_pad = timed_calls(pad_call, 1000, stream)
+        result["empty_launch_us_all_pad"] = round(t_pad * 1e3, 3)
+        say(f"empty launch: {t_empty * 1e3:.2f} us (stream), {t_graph * 1e3:.2f} us (graph), "
+            f"{t_pad * 1e3:.2f} us (all {spec.B} listed, every source the pad slot)")
 
     if not args.no_cpu_baseline:
         say(f"CPU oracle sample (~{args.cpu_seconds:.0f} s)")
