@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="profile mode: warmup + timed steps only")
     ap.add_argument("--empty-only", action="store_true", help="profile mode: 200 calls with no active request")
+    ap.add_argument("--all-pad-only", action="store_true",
+                    help="profile mode: 200 calls with every request listed and every source the pad slot")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="counter mode: 2 full-batch calls, then 2 plain device copies of 1 GiB")
     ap.add_argument("--workload", default=WORKLOAD, choices=["large_bf16", "large_i8", "large_f8sr"],
@@ -175,7 +177,8 @@ def main():
     if args.only_ssu:
         print(json.dumps({"ssu_decode": ssu_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
         return
-    profile_mode = args.only_main or args.empty_only or args.pmc_calibrate or args.only_checkpoints
+    profile_mode = (args.only_main or args.empty_only or args.all_pad_only or args.pmc_calibrate
+                    or args.only_checkpoints)
     wl = args.workload if profile_mode else WORKLOAD
     spec = ri.CONFIGS[wl]
     say("generating", wl, "seed", SEEDS[wl])
@@ -197,11 +200,16 @@ def main():
         print(json.dumps({"checkpoints": checkpoint_workload(dp, tabs, spec, stream, args.steps)}), flush=True)
         return
 
-    if args.empty_only or args.pmc_calibrate:
+    if args.empty_only or args.all_pad_only or args.pmc_calibrate:
         if args.empty_only:
             empty = torch.full((spec.B,), -1, dtype=torch.int32, device=dev)
             for _ in range(200):
                 call(empty)
+        elif args.all_pad_only:
+            pad_src = torch.full((spec.L, spec.B), spec.pad_slot_id, dtype=torch.int32, device=dev)
+            pad_call = hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "src_slots": pad_src}))
+            for _ in range(200):
+                pad_call()
         else:
             for _ in range(2):
                 call()

@@ -96,6 +96,47 @@ __device__ __forceinline__ int count_active(const int32_t* active, int B, int la
   return B;
 }
 
+// Liveness of 64 chunks of one wavefront at once, one chunk per lane: lane j
+// tests chunk gw + (qb + j) * tw.  A chunk inside one (request, layer) is live
+// unless the pair is skipped (a pad or negative source; for NCK = 1 a pad
+// destination; for several checkpoints every destination the pad slot).  A
+// chunk that spans several pairs is reported live and left to the main loop.
+// Returns the ballot of live chunks; lanes past the last item are not live.
+// Every entry read is in range: i < n_active, and count_active stops at the
+// first entry outside [0, B).
+template <int NCK>
+__device__ __forceinline__ uint64_t live_chunks(const KernelArgs& a, int64_t gw, int64_t tw, int64_t qb,
+                                                int64_t csz, int64_t items, int lane) {
+  const int64_t it0 = (gw + (qb + lane) * tw) * csz;
+  bool live = false;
+  if (it0 < items) {
+    const int64_t il0 = it0 / a.H;
+    const int64_t il1 = (min(items, it0 + csz) - 1) / a.H;
+    if (il0 != il1) {
+      live = true;
+    } else {
+      const int i = static_cast<int>(il0 / a.L);
+      const int l = static_cast<int>(il0 - static_cast<int64_t>(i) * a.L);
+      const int b = gload(a.active + i);
+      const int64_t lb = static_cast<int64_t>(l) * a.B + b;
+      const int s = gload(a.src_slots + lb);
+      bool any_dst = false;
+      if constexpr (NCK == 1) {
+        const int d = gload(a.dst_slots + lb);
+        any_dst = d != a.pad && d >= 0;
+      } else {
+        const int64_t LB = static_cast<int64_t>(a.L) * a.B;
+        for (int c = 0; c < a.ncp; ++c) {
+          const int d = gload(a.dst_slots + c * LB + lb);
+          any_dst = any_dst || (d != a.pad && d >= 0);
+        }
+      }
+      live = s != a.pad && s >= 0 && any_dst;
+    }
+  }
+  return __ballot(live);
+}
+
 // An fp32 row chunk held as two 4-column halves half a row apart (columns
 // c..c+3 and c+64..c+67 of a 128-column row): with lane cc of a row at
 // c = 4*cc, each 16-byte access instruction covers contiguous bytes across
@@ -360,10 +401,19 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
   constexpr int64_t kC = Tune::kChunkItems;
   const int64_t csz = kC == 0 ? 0 : min(kC, (items + tw - 1) / tw);
   int64_t chunk = gw, it, end;
+  // When some wavefront deals several chunks, each wavefront first tests its
+  // next 64 chunks in parallel (live_chunks) and walks only the live ones, so
+  // skipped (request, layer) pairs cost no round trips of their own: a call
+  // whose listed requests are all padded costs about one near-empty launch.
+  const bool filt = kC > 0 && (items + csz - 1) / csz > tw;
+  int64_t qb = 0;       // position in this wavefront's chunk sequence of lane 0 of the batch
+  uint64_t live = 0;    // live chunks of the batch not yet taken
   if constexpr (kC == 0) {
     const int64_t per = items / tw, rem = items % tw;
     it = gw * per + (gw < rem ? gw : rem);
     end = it + per + (gw < rem ? 1 : 0);
+  } else if (filt) {
+    it = end = 0;  // the first chunk comes from the filter
   } else {
     it = chunk * csz;
     end = min(items, it + csz);
@@ -381,7 +431,19 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
   for (;;) {
     if (it >= end) {
       if constexpr (kC == 0) break;
-      chunk += tw;
+      if (filt) {
+        while (live == 0) {
+          if ((gw + qb * tw) * csz >= items) break;
+          live = live_chunks<NCK>(a, gw, tw, qb, csz, items, lane);
+          if (live == 0) qb += 64;
+        }
+        if (live == 0) break;
+        chunk = gw + (qb + __builtin_ctzll(live)) * tw;
+        live &= live - 1;
+        if (live == 0) qb += 64;
+      } else {
+        chunk += tw;
+      }
       it = chunk * csz;
       if (it >= items) break;
       end = min(items, it + csz);

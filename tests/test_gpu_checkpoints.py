@@ -72,6 +72,23 @@ def test_checkpoints_against_oracle(dev, state, rounds, n_ck, in_place):
     parity.check_checkpoints_against_oracle(prob, dst, pre, st, sc)
 
 
+@pytest.mark.parametrize("H", [8, 24])
+def test_checkpoints_mixed_pads_many_chunks_per_wave(dev, H):
+    """Pad sources and pad checkpoint destinations mixed with live pairs on
+    grids of 1-3 workgroups, so each wavefront deals many chunks and skips
+    dead ones from its batched liveness test (H = 24: chunks straddle pairs)."""
+    import parity
+    spec = ri.with_(CK, L=6, B=24, H=H, hpg=8, dim=64, dstate=128, slots=96, ring_slots=96, n_active=22,
+                    state_dtype="bf16", input_dtype="bf16", pad_frac=0.5)
+    seed = 3090 + H
+    prob = ri.make_problem(spec, seed)
+    dst, pre = ri.make_checkpoints(spec, prob.meta, seed + 1, 3, in_place=True, k0_frac=0.2, pad_frac=0.6)
+    for mw in (1, 3):
+        say("checkpoints mixed pads H", H, "grid", mw, "seed", seed)
+        st, sc = run_checkpoints(prob, dst, pre, dev, max_workgroups=mw)
+        parity.check_checkpoints_against_oracle(prob, dst, pre, st, sc)
+
+
 def test_checkpoints_window_16_wrapping_ring(dev):
     import parity
     spec = ri.with_(CK, W=16, R=5, k_lo=0, k_hi=16, state_dtype="bf16", input_dtype="f16", philox_rounds=10)

@@ -143,6 +143,33 @@ def test_all_pad_and_nondefault_pad(dev):
     check(prob2, dev)
 
 
+@pytest.mark.parametrize("H,hpg", [(8, 4), (4, 2), (24, 8)])
+@pytest.mark.parametrize("pad_frac", [0.5, 0.97])
+def test_mixed_pads_many_chunks_per_wave(dev, H, hpg, pad_frac):
+    """Padded (layer, request) pairs mixed with live ones while each wavefront
+    deals many chunks: grids of 1-7 workgroups give up to 100+ chunks per
+    wavefront, so the kernel tests chunk liveness in several batches of 64
+    and skips dead ones.  H = 4 and 24 make chunks of 16 heads straddle
+    (request, layer) pairs; pad_frac 0.97 leaves whole batches dead."""
+    spec = ri.with_(MATRIX, L=8, B=40, H=H, hpg=hpg, dim=16, dstate=16, slots=80, ring_slots=80,
+                    n_active=36, pad_frac=pad_frac, stride_pad="per_layer")
+    prob = ri.make_problem(spec, 2310 + H + int(pad_frac * 100))
+    for mw in (1, 3, 7, 0):
+        say("mixed pads H", H, "pad_frac", pad_frac, "grid", mw)
+        check(prob, dev, max_workgroups=mw)
+
+
+def test_all_listed_all_pad_many_chunks(dev):
+    """Every listed request padded in every layer, with enough items that each
+    wavefront of the default grid deals several chunks: nothing is written."""
+    spec = ri.with_(MATRIX, L=48, B=48, H=32, hpg=8, dim=16, dstate=16, slots=96, ring_slots=96,
+                    n_active=48, pad_frac=1.0, stride_pad="none")
+    prob = ri.make_problem(spec, 2320)
+    for mw in (0, 2):
+        say("all listed, all padded; grid", mw)
+        check(prob, dev, max_workgroups=mw)
+
+
 def test_entries_after_first_terminator_ignored(dev):
     prob = ri.make_problem(ri.with_(MATRIX, n_active=3), 2303)
     prob.meta.active[1] = -1                  # only the first request counts
