@@ -195,6 +195,19 @@ rssm_status rssm_debug_encode_rows(const rssm_materialize_desc *desc, const floa
                                    void *out_codes, float *out_scales, int32_t n,
                                    void *hip_stream);
 
+/* Test hook: the row quantization parameters the one-byte encode uses, for
+ * n given row maxima.  For a row whose largest magnitude is m (rowmax[i] =
+ * m >= 0): scale[i] = m / qmax and inv[i] = qmax / m as correctly rounded
+ * fp32 quotients, qmax = 127 (RSSM_I8) or 448 (RSSM_F8E4M3); a row with
+ * m = 0, m infinite or qmax / m not finite gets scale 0 (inv is then the
+ * IEEE quotient and unused by the encode).  This is the pull-request page's
+ * per-row destination scale ("Replayssm prefix materialize", change table:
+ * external decode-scale input, writes the destination scale buffer).
+ * rowmax, scale, inv: device fp32 [n]; n >= 0 (0 enqueues nothing);
+ * state_dtype other than RSSM_I8 / RSSM_F8E4M3 is RSSM_ERR_INVALID_ARGUMENT. */
+rssm_status rssm_debug_row_scales(int32_t state_dtype, const float *rowmax, float *scale, float *inv,
+                                  int32_t n, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

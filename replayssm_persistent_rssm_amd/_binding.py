@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "librssm_materialize.so")
 RSSM_F32, RSSM_BF16, RSSM_F16, RSSM_I8, RSSM_F8E4M3 = 0, 1, 2, 3, 4
 RSSM_OK, RSSM_ERR_INVALID_ARGUMENT, RSSM_ERR_UNSUPPORTED, RSSM_ERR_HIP = 0, 1, 2, 3
 EXPORTS = ("rssm_materialize", "rssm_materialize_checkpoints", "rssm_last_error", "rssm_materialize_launch_config",
-           "rssm_debug_encode_rows", "rssm_gdn_commit", "rssm_ssu_decode", "rssm_pool_alloc", "rssm_pool_free",
+           "rssm_debug_encode_rows", "rssm_debug_row_scales", "rssm_gdn_commit", "rssm_ssu_decode", "rssm_pool_alloc", "rssm_pool_free",
            "rssm_torch_pool_alloc", "rssm_torch_pool_free")
 RSSM_MAX_CHECKPOINTS = 4
 RSSM_SSU_MAX_TOKENS = 8
@@ -105,6 +105,9 @@ def _load():
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.c_void_p]
     lib.rssm_debug_encode_rows.restype = ctypes.c_int
+    lib.rssm_debug_row_scales.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.c_void_p]
+    lib.rssm_debug_row_scales.restype = ctypes.c_int
     return lib
 
 
@@ -488,6 +491,16 @@ def rssm_debug_encode_rows(rows, coords, rand_seed, out_codes, out_scales, *, st
         _ptr(rand_seed, "rand_seed", torch.int64, (1,)) if rand_seed is not None else None,
         _ptr(out_codes, "out_codes"), _ptr(out_scales, "out_scales") if out_scales is not None else None,
         n, _stream_handle(stream)))
+
+
+def rssm_debug_row_scales(rowmax, scale, inv, *, state_dtype, stream=None) -> None:
+    """Row scale and inverse scale of the one-byte encode for row maxima [n] (test hook)."""
+    import torch
+    n = int(rowmax.shape[0])
+    _check(_lib.rssm_debug_row_scales(
+        dtype_code(state_dtype), _ptr(rowmax, "rowmax", torch.float32, (n,)),
+        _ptr(scale, "scale", torch.float32, (n,)), _ptr(inv, "inv", torch.float32, (n,)), n,
+        _stream_handle(stream)))
 
 
 def pointer_table(tensors: Sequence, device) -> "torch.Tensor":

@@ -162,8 +162,9 @@ __device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_
   constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
   const uint64_t p0 = static_cast<uint64_t>(kM0) * c0;
   const uint64_t p1 = static_cast<uint64_t>(kM1) * c2;
-  const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-  const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+  // Three-way XORs as one gfx950 bitop3 each (truth table 0x96 = a ^ b ^ c).
+  const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1, k0, 0x96);
+  const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3, k1, 0x96);
   c1 = static_cast<uint32_t>(p1);
   c3 = static_cast<uint32_t>(p0);
   c0 = n0;
@@ -203,6 +204,64 @@ __device__ __forceinline__ void sr_words(uint32_t (&u)[8], int r, int c0, int ds
   const uint32_t base = static_cast<uint32_t>((static_cast<int64_t>(r) * dstate + c0) >> 2);
   philox4x32_pair(base, static_cast<uint32_t>(h), static_cast<uint32_t>(b), static_cast<uint32_t>(l), k0, k1,
                   rounds, u);
+}
+
+// ---------------------------------------------------------------------------
+// Byte packing.  v_perm_b32 (operands s0, s1) builds each result byte from a
+// selector byte: 0-3 pick bytes 0-3 of s1, 4-7 bytes 0-3 of s0, 0x0c gives 0.
+// ---------------------------------------------------------------------------
+// Byte 0 of a, b, c, d as one little-endian word (three byte permutes).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Byte 3 of a, b, c, d as one little-endian word (bit 7 of each byte is the
+// sign bit of the corresponding fp32 value).
+__device__ __forceinline__ uint32_t pack_high_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0703u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0703u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// ---------------------------------------------------------------------------
+// Per-row symmetric quantization parameters: scale = m / qmax and
+// inv = qmax / m, both correctly rounded fp32 quotients, for a row whose
+// largest magnitude is m.  A row is valid when m > 0, m is finite and inv is
+// finite; an invalid row gets scale 0 (its codes are zero).
+//
+// For 2^-100 <= m <= 2^100 both quotients come from short fma sequences with
+// a single exact-residual correction:
+//   scale: s = m * c with c = RN(1/qmax), then s + (m - s*qmax) * c;
+//   inv:   y = rcp(m) refined by one Newton step, q = qmax * y, then
+//          q + (qmax - m*q) * y.
+// Both equal the IEEE quotient for every fp32 m in that range, qmax 127 or
+// 448: checked exhaustively against division (scale on the host for every
+// m >= 2^-120; inv on gfx950 for all 1.68e9 values of the range).  A
+// wavefront with any row outside the range uses the divisions.  All lanes of
+// the wavefront must execute this.
+// ---------------------------------------------------------------------------
+template <int QMAX>
+__device__ __forceinline__ bool row_quant(float m, float& scale, float& inv) {
+  static_assert(QMAX == 127 || QMAX == 448, "qmax");
+  constexpr float q = static_cast<float>(QMAX);
+  constexpr float c = (QMAX == 127) ? 0x1.020408p-7f : 0x1.24924ap-9f;  // RN(1 / qmax)
+  static_assert(c == 1.0f / q, "c must be the correctly rounded reciprocal of qmax");
+  const bool fast = (m >= 0x1p-100f) && (m <= 0x1p100f);
+  if (__builtin_expect(__ballot(!fast) == 0, 1)) {
+    const float s0 = m * c;
+    scale = fmaf(fmaf(-s0, q, m), c, s0);
+    const float y0 = __builtin_amdgcn_rcpf(m);
+    const float y1 = fmaf(fmaf(-m, y0, 1.0f), y0, y0);
+    const float q0 = q * y1;
+    inv = fmaf(fmaf(-m, q0, q), y1, q0);
+    return true;
+  }
+  inv = q / m;
+  const bool ok = (m > 0.0f) && !__builtin_isinf(m) && __builtin_isfinite(inv);
+  scale = ok ? m / q : 0.0f;
+  return ok;
 }
 
 // ---------------------------------------------------------------------------
@@ -277,13 +336,14 @@ __device__ __forceinline__ uint32_t e4m3_sr(float t, uint32_t u) {
   return sign | (a >= 0x1p-6f ? code_n : code_s);
 }
 
-// e4m3_sr for 2^-6 <= |t| < 464 only: the normal-range rule without the
-// subnormal candidate (callers check the range for the whole wave first).
-__device__ __forceinline__ uint32_t e4m3_sr_normal(float t, uint32_t u) {
+// Magnitude code (sign bit clear) of e4m3_sr for 2^-6 <= |t| < 464 only: the
+// normal-range rule without the subnormal candidate (callers check the range
+// for the whole wave first).  bits << 12 is the 20 dropped mantissa bits at
+// the top of the word; bits 30..20 are the exponent and the kept mantissa.
+__device__ __forceinline__ uint32_t e4m3_sr_normal_mag(float t, uint32_t u) {
   const uint32_t bits = __float_as_uint(t);
-  const uint32_t mag = bits & 0x7FFFFFFFu;
-  const uint32_t up = (u < ((mag & 0xFFFFFu) << 12)) ? 1u : 0u;
-  return ((bits >> 24) & 0x80u) | min((mag >> 20) - 960u + up, 0x7Eu);
+  const uint32_t up = (u < (bits << 12)) ? 1u : 0u;
+  return min(((bits >> 20) & 0x7FFu) - 960u + up, 0x7Eu);
 }
 
 // General e4m3 rounding (any input): nearest-even or stochastic, saturating;

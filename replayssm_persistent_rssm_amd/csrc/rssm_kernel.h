@@ -207,49 +207,49 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
       out.w[i] = f16_round(acc[2 * i], SR, u[2 * i]) | (f16_round(acc[2 * i + 1], SR, u[2 * i + 1]) << 16);
   } else {
     // Per-row symmetric quantization: scale = rowmax/qmax, t = v * (qmax/rowmax),
-    // both IEEE fp32 divisions.  An all-zero row (or one whose inverse
-    // overflows) stores scale 0 and zero codes.
-    constexpr float qmax = (ST == kI8) ? 127.0f : 448.0f;
+    // both correctly rounded fp32 quotients (row_quant).  An all-zero row (or
+    // one whose inverse overflows) stores scale 0 and zero codes.
+    constexpr int qmax = (ST == kI8) ? 127 : 448;
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(acc[i]));
     m = row16_max(m);
-    const float inv = qmax / m;
-    const bool ok = (m > 0.0f) && !__builtin_isinf(m) && __builtin_isfinite(inv);
-    row_scale = ok ? m / qmax : 0.0f;
+    float inv;
+    const bool ok = row_quant<qmax>(m, row_scale, inv);
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = acc[i] * inv;
-    if constexpr (ST == kI8) {
-      uint32_t code[8];
+    // Whether any lane of the wavefront holds a NaN element (wave-uniform).
+    auto any_nan = [&t]() {
       bool has_nan = false;
 #pragma unroll
       for (int i = 0; i < 8; ++i) has_nan |= (t[i] != t[i]);
-      if (SR || __builtin_expect(__ballot(has_nan) != 0, 0)) {
+      return __builtin_expect(__ballot(has_nan) != 0, 0);
+    };
+    if constexpr (ST == kI8) {
+      uint32_t code[8];
+      if (SR || any_nan()) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) code[i] = i8_round(t[i], SR, u[i]);
       } else {
-        // Nearest-even on [-127, 127]: after the clamp, adding 1.5 * 2^23
-        // rounds to an integer in one IEEE rounding, and the low byte of the
-        // sum's bits is the two's-complement code.
+        // Nearest-even.  In a valid row |t| <= 127 (1 + 2^-24)^2 < 127.5, so
+        // adding 1.5 * 2^23 rounds t to an integer in [-127, 127] in one IEEE
+        // rounding with no clamp, and the low byte of the sum's bits is the
+        // two's-complement code.  An invalid row is zeroed below.
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          code[i] = __float_as_uint(__builtin_amdgcn_fmed3f(t[i], -127.0f, 127.0f) + 12582912.0f) & 0xFFu;
+        for (int i = 0; i < 8; ++i) code[i] = __float_as_uint(t[i] + 12582912.0f);
       }
-      out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-      out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+      out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
+      out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
     } else {
       // |t| <= 448(1 + 2^-22) for every finite element of a valid row.  NaN
       // elements (ignored by the row max) take the general path.
-      bool has_nan = false;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) has_nan |= (t[i] != t[i]);
-      if (__builtin_expect(__ballot(has_nan) != 0, 0)) {
+      if (any_nan()) {
         uint32_t code[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) code[i] = e4m3_round(t[i], SR, u[i]);
-        out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-        out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+        out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
+        out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
       } else if constexpr (SR) {
         uint32_t code[8];
         bool has_sub = false;
@@ -258,12 +258,21 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
         if (__ballot(has_sub) != 0) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) code[i] = e4m3_sr(t[i], u[i]);
+          out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
+          out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
         } else {
+          // Magnitude codes, then the sign bits: bit 7 of byte 3 of each fp32
+          // value is its sign, which goes to bit 7 of its code byte.
 #pragma unroll
-          for (int i = 0; i < 8; ++i) code[i] = e4m3_sr_normal(t[i], u[i]);
+          for (int i = 0; i < 8; ++i) code[i] = e4m3_sr_normal_mag(t[i], u[i]);
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t sg = pack_high_bytes(__float_as_uint(t[4 * w]), __float_as_uint(t[4 * w + 1]),
+                                                __float_as_uint(t[4 * w + 2]), __float_as_uint(t[4 * w + 3]));
+            out.w[w] = (sg & 0x80808080u) |
+                       pack_low_bytes(code[4 * w], code[4 * w + 1], code[4 * w + 2], code[4 * w + 3]);
+          }
         }
-        out.w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-        out.w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
       } else {
         // Hardware nearest-even conversion: equal to e4m3_round for |t| < 464
         // (checked on gfx950), which covers every finite row-scaled value.
@@ -840,6 +849,21 @@ __global__ void __launch_bounds__(kBlock) encode_rows_kernel(const float* rows, 
     if constexpr (kOneByte<ST>) {
       if (cc == 0) gstore(out_scales + row, rs);
     }
+  }
+}
+
+// Test hook: scale and inverse scale of row_quant<QMAX> for given row maxima
+// (rowmax[i] >= 0), one per lane, in wavefronts of 64 consecutive rows.
+template <int QMAX>
+__global__ void __launch_bounds__(kBlock) row_scales_kernel(const float* rowmax, float* scale, float* inv,
+                                                            int32_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const float m = (i < n) ? gload(rowmax + i) : 1.0f;
+  float s, q;
+  row_quant<QMAX>(m, s, q);
+  if (i < n) {
+    gstore(scale + i, s);
+    gstore(inv + i, q);
   }
 }
 

@@ -614,4 +614,24 @@ rssm_status rssm_debug_encode_rows(const rssm_materialize_desc* desc, const floa
   return RSSM_OK;
 }
 
+rssm_status rssm_debug_row_scales(int32_t state_dtype, const float* rowmax, float* scale, float* inv, int32_t n,
+                                  void* hip_stream) {
+  g_err[0] = '\0';
+  if (state_dtype != RSSM_I8 && state_dtype != RSSM_F8E4M3)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "state_dtype must be a one-byte state (I8 or F8E4M3), got %d",
+                state_dtype);
+  if (n < 0) return fail(RSSM_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  if (n == 0) return RSSM_OK;
+  if (rowmax == nullptr || scale == nullptr || inv == nullptr)
+    return fail(RSSM_ERR_INVALID_ARGUMENT, "rowmax, scale and inv must not be NULL");
+  const void* fn = state_dtype == RSSM_I8 ? reinterpret_cast<const void*>(&rssm::row_scales_kernel<127>)
+                                          : reinterpret_cast<const void*>(&rssm::row_scales_kernel<448>);
+  const int grid = static_cast<int>((static_cast<int64_t>(n) + rssm::kBlock - 1) / rssm::kBlock);
+  void* params[] = {&rowmax, &scale, &inv, &n};
+  hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(rssm::kBlock), params, 0,
+                                   static_cast<hipStream_t>(hip_stream));
+  if (err != hipSuccess) return fail(RSSM_ERR_HIP, "launch of row_scales_kernel failed: %s", hipGetErrorString(err));
+  return RSSM_OK;
+}
+
 }  // extern "C"

@@ -120,6 +120,15 @@ def test_debug_encode_rows_validation(rp):
     assert rp.lib().rssm_debug_encode_rows(ctypes.byref(d), None, None, None, None, None, 0, None) == 0
 
 
+def test_debug_row_scales_validation(rp):
+    lib = rp.lib()
+    assert lib.rssm_debug_row_scales(rp.RSSM_BF16, 0x10000, 0x10000, 0x10000, 4, None) == 1
+    assert "one-byte" in rp.rssm_last_error()
+    assert lib.rssm_debug_row_scales(rp.RSSM_I8, 0x10000, 0x10000, 0x10000, -1, None) == 1
+    assert lib.rssm_debug_row_scales(rp.RSSM_F8E4M3, None, 0x10000, 0x10000, 4, None) == 1
+    assert lib.rssm_debug_row_scales(rp.RSSM_I8, None, None, None, 0, None) == 0
+
+
 def test_caller_examples_from_the_pages(rp):
     rows = [l.split() for l in open(os.path.join(ROOT, "tests", "golden", "caller_examples.txt"))
             if l.strip() and not l.startswith("#")]

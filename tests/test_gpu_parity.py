@@ -288,6 +288,10 @@ def test_debug_encode_rows_bit_exact(dev, state, rounds, dstate):
     rows[2, :] = np.float32(2.0 ** -130)               # fp32 subnormal
     rows[3, :dstate // 2] = np.float32(70000.0)        # fp16 overflow / saturation
     rows[4] = rng.standard_normal(dstate).astype(np.float32) * 1e-8
+    # row maxima at the edges of the short quotient sequences' range [2^-100, 2^100]
+    for i, top in zip(range(5, 10), (2.0 ** 100, 2.0 ** -100, 2.0 ** -101, 2.0 ** 101, 3.0e38)):
+        rows[i] = (rng.uniform(-1, 1, dstate) * top).astype(np.float32)
+        rows[i, 7] = np.float32(top)
     coords = np.stack([rng.integers(0, 48, n), rng.integers(0, 256, n), rng.integers(0, 256, n),
                        rng.integers(0, 64, n)], 1).astype(np.int32)
     seed = 0x123456789ABCDEF
@@ -309,6 +313,39 @@ def test_debug_encode_rows_bit_exact(dev, state, rounds, dstate):
         assert np.array_equal(got[i], codes.view(np.uint8)), f"row {i} ({l},{b},{h},{r})"
         if scales is not None:
             assert np.float32(scales[i].item()).view(np.uint32) == np.float32(scale).view(np.uint32), f"row {i} scale"
+
+
+def test_row_scales_correctly_rounded(dev):
+    """The one-byte encode's row scale m/qmax and inverse qmax/m equal IEEE
+    fp32 division (numpy float32) bit for bit: every mantissa at exponents on
+    both sides of the short sequences' range [2^-100, 2^100] and at the ends
+    of the normal range, the first 2^20 subnormals, and special values."""
+    import torch
+    from replayssm_persistent_rssm_amd import rssm_debug_row_scales
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    parts = [((np.uint32(e + 127) << np.uint32(23)) | mant).view(np.float32)
+             for e in (-126, -120, -101, -100, -1, 0, 99, 100, 127)]
+    parts.append(np.arange(1, 1 << 20, dtype=np.uint32).view(np.float32))
+    parts.append(np.array([0.0, 2.0 ** -100, 2.0 ** 100, np.finfo(np.float32).max, np.inf], np.float32))
+    m = np.concatenate(parts)
+    d_m = torch.from_numpy(m).to(dev)
+    for state, q in (("i8", 127), ("f8e4m3", 448)):
+        say("row scales", state, "values", m.size)
+        scale = torch.empty_like(d_m)
+        inv = torch.empty_like(d_m)
+        rssm_debug_row_scales(d_m, scale, inv, state_dtype=state)
+        torch.cuda.synchronize()
+        with np.errstate(divide="ignore", over="ignore"):
+            want_inv = np.float32(q) / m
+            want_scale = m / np.float32(q)
+        ok = (m > 0) & np.isfinite(m) & np.isfinite(want_inv)
+        want_scale = np.where(ok, want_scale, np.float32(0)).astype(np.float32)
+        got_s = scale.cpu().numpy()
+        got_i = inv.cpu().numpy()
+        bad_s = np.flatnonzero(got_s.view(np.uint32) != want_scale.view(np.uint32))
+        assert bad_s.size == 0, f"{state}: {bad_s.size} scales differ, first m={m[bad_s[0]]!r}"
+        bad_i = np.flatnonzero(ok & (got_i.view(np.uint32) != want_inv.view(np.uint32)))
+        assert bad_i.size == 0, f"{state}: {bad_i.size} inverses differ, first m={m[bad_i[0]]!r}"
 
 
 # --------------------------------------------------------------------------
