@@ -306,13 +306,25 @@ __device__ __forceinline__ int ring_entry(int r0, int j, int R) {
   return e;
 }
 
-// Resident wavefronts per SIMD the register budget is sized for: B_j for 8
-// columns costs 8*KMAX registers per lane.
+// B_j rows held in registers: 8 columns cost 8 registers per token.  Windows
+// of up to 8 tokens keep every row in registers; 16-token windows keep the
+// first 4 and read the other 12 from the wavefront's LDS.  On MI355X that
+// trade (LDS reads for registers) lets the 16-token instances run 4 waves per
+// SIMD instead of 2: the e4m3 + Philox workload (windows up to 16) ran 19%
+// faster than with all 16 rows in registers; 8 rows in registers at 3 waves
+// gained 14%.  For int8 with 8-token windows, 4 rows in LDS ran 5% slower.
+template <int KMAX> constexpr int kBRegs = (KMAX > 8) ? 4 : KMAX;
+
+// Resident wavefronts per SIMD the register budget is sized for.
 // e4m3 state adds software decode/encode on top of the row scales: its
 // 8-token instances get a 3-wave budget (168 registers) so they do not spill.
 // int8 keeps 4 waves: it runs ~11% faster than with 3 waves on MI355X,
 // although the compiler then spills a few registers outside the fold.
-template <int KMAX, int ST> constexpr int kWavesPerSimd = (KMAX > 8) ? 2 : ((ST == kF8) ? 3 : 4);
+// 16-token instances get 4 waves, except with fp32 x/B (16 raw 32-byte B
+// chunks are held while a group's rows load) and the multi-checkpoint
+// instances (segment bookkeeping): 3 waves, where they do not spill.
+template <int KMAX, int ST, int IT, int NCK>
+constexpr int kWavesPerSimd = (KMAX > 8) ? ((IT == kF32 || NCK > 1) ? 3 : 4) : ((ST == kF8) ? 3 : 4);
 
 // Knobs of the state stream.  The library's instances use the defaults; the
 // alternatives exist so that streaming patterns can be compared on hardware.
@@ -332,9 +344,9 @@ struct DefaultTune {
   static constexpr int kWavesPerSimd = 0;      // register budget; 0: the rule above
 };
 
-template <class Tune, int KMAX, int ST>
+template <class Tune, int KMAX, int ST, int IT, int NCK>
 constexpr int waves_per_simd() {
-  return Tune::kWavesPerSimd > 0 ? Tune::kWavesPerSimd : kWavesPerSimd<KMAX, ST>;
+  return Tune::kWavesPerSimd > 0 ? Tune::kWavesPerSimd : kWavesPerSimd<KMAX, ST, IT, NCK>;
 }
 
 // Checkpoint bookkeeping of one (request, layer): kc[c] is the prefix length of
@@ -365,7 +377,7 @@ __device__ __forceinline__ void sort_checkpoints(int (&kc)[NCK], int (&dc)[NCK])
 // relative to the end of their segment: over segment [k', k''),
 // S_k'' = (prod_{k'<=u<k''} a_u) S_k' + sum_{k'<=j<k''} dt_j (prod_{j<u<k''} a_u) x_j B_j^T.
 template <int ST, int IT, int DIM, int DSTATE, int KMAX, bool SR, int NCK = 1, class Tune = DefaultTune>
-__global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) materialize_kernel(const KernelArgs a) {
+__global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NCK>())) materialize_kernel(const KernelArgs a) {
   constexpr int TPR = DSTATE / 8;                 // lanes per state row
   constexpr int RPP = 64 / TPR;                   // rows per pass of a wavefront
   constexpr int NPASS = (DIM + RPP - 1) / RPP;    // passes per tile
@@ -387,10 +399,14 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
   static_assert(NCK >= 1 && NCK <= 4, "NCK");
 
   __shared__ __attribute__((aligned(16))) float lds_wx[kWaves][DIM * KMAX];
+  constexpr int KREG = kBRegs<KMAX>;   // B rows of tokens below KREG in registers
+  constexpr int KLDS = KMAX - KREG;     // the others in this wavefront's LDS, [token - KREG][column]
+  __shared__ __attribute__((aligned(16))) float lds_B[kWaves][KLDS > 0 ? KLDS * DSTATE : 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
   float* wx = lds_wx[wave];
+  float* bl = lds_B[wave];
   const int cc = lane % TPR;
   const int rr = lane / TPR;
   constexpr int PS = RPP * DSTATE * SB;  // bytes between passes of a tile
@@ -594,10 +610,12 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
     }
 
     for (int g = h0 / a.hpg; g * a.hpg < h1; ++g) {
-      // B_j for this lane's 8 columns, shared by the heads of group g.  All
-      // KMAX rows are requested at once (tokens past k re-read entry r0 and
-      // are then zeroed), so the group costs one round trip, not k.
-      float Bv[KMAX][8];
+      // B_j for this lane's 8 columns, shared by the heads of group g: tokens
+      // below KREG in registers, the others in the wavefront's LDS (written by
+      // the lanes of row 0 of each pass).  All KMAX rows are requested at once
+      // (tokens past k re-read entry r0 and are then zeroed), so the group
+      // costs one round trip, not k.
+      float Bv[KREG][8];
       {
         Chunk<IT> braw[KMAX];
 #pragma unroll
@@ -605,13 +623,26 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
           const int e = ring_entry(r0, j < k ? j : 0, a.R);
           braw[j] = load_chunk<IT>(B_slot + ((static_cast<int64_t>(e) * G + g) * DSTATE + cc * 8) * IB);
         }
+        if constexpr (KLDS > 0) wave_lds_fence();  // the previous group's reads of bl are done
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
-          decode_chunk<IT>(braw[j], Bv[j]);
+          float v[8];
+          decode_chunk<IT>(braw[j], v);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) Bv[j][q] = (j < k) ? Bv[j][q] : 0.0f;
+          for (int q = 0; q < 8; ++q) v[q] = (j < k) ? v[q] : 0.0f;
+          if (j < KREG) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) Bv[j < KREG ? j : 0][q] = v[q];
+          } else if (rr == 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) bl[(j >= KREG ? j - KREG : 0) * DSTATE + cc * 8 + q] = v[q];
+          }
         }
       }
+      // B_j[c] of this lane's columns (j and c are compile-time after unrolling).
+      auto Bat = [&](int j, int c) -> float {
+        return j < KREG ? Bv[j < KREG ? j : 0][c] : bl[(j >= KREG ? j - KREG : 0) * DSTATE + cc * 8 + c];
+      };
       const int hb = max(h0, g * a.hpg);
       const int he = min(h1, (g + 1) * a.hpg);
       for (int h = hb; h < he; ++h) {
@@ -732,10 +763,10 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
                     const float4 w4 = *reinterpret_cast<const float4*>(wrow + jb * 4);
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
-                      acc[c] = fmaf(w4.x, Bv[jb * 4 + 0][c], acc[c]);
-                      acc[c] = fmaf(w4.y, Bv[jb * 4 + 1][c], acc[c]);
-                      acc[c] = fmaf(w4.z, Bv[jb * 4 + 2][c], acc[c]);
-                      acc[c] = fmaf(w4.w, Bv[jb * 4 + 3][c], acc[c]);
+                      acc[c] = fmaf(w4.x, Bat(jb * 4 + 0, c), acc[c]);
+                      acc[c] = fmaf(w4.y, Bat(jb * 4 + 1, c), acc[c]);
+                      acc[c] = fmaf(w4.z, Bat(jb * 4 + 2, c), acc[c]);
+                      acc[c] = fmaf(w4.w, Bat(jb * 4 + 3, c), acc[c]);
                     }
                   }
                 }
@@ -780,10 +811,10 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
                           // whole block inside (tokens past k carry -0 weights)
 #pragma unroll
                           for (int c = 0; c < 8; ++c) {
-                            acc[c] = fmaf(w4.x, Bv[t0 + 0][c], acc[c]);
-                            acc[c] = fmaf(w4.y, Bv[t0 + 1][c], acc[c]);
-                            acc[c] = fmaf(w4.z, Bv[t0 + 2][c], acc[c]);
-                            acc[c] = fmaf(w4.w, Bv[t0 + 3][c], acc[c]);
+                            acc[c] = fmaf(w4.x, Bat(t0 + 0, c), acc[c]);
+                            acc[c] = fmaf(w4.y, Bat(t0 + 1, c), acc[c]);
+                            acc[c] = fmaf(w4.z, Bat(t0 + 2, c), acc[c]);
+                            acc[c] = fmaf(w4.w, Bat(t0 + 3, c), acc[c]);
                           }
                         } else {
                           // block cut by a segment boundary: only its own tokens
@@ -792,7 +823,7 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST>())) ma
                           for (int t = 0; t < 4; ++t) {
                             if (t0 + t >= prev && t0 + t < kend) {
 #pragma unroll
-                              for (int c = 0; c < 8; ++c) acc[c] = fmaf(wt[t], Bv[t0 + t][c], acc[c]);
+                              for (int c = 0; c < 8; ++c) acc[c] = fmaf(wt[t], Bat(t0 + t, c), acc[c]);
                             }
                           }
                         }

@@ -266,9 +266,11 @@ struct LaunchCache {
 };
 thread_local LaunchCache g_last;
 
-int lds_bytes_of(const rssm_materialize_desc* d) {
-  const int kmax = d->max_window <= 8 ? 8 : 16;
-  return rssm::kWaves * d->dim * kmax * static_cast<int>(sizeof(float));
+// Static LDS of a compiled kernel instance, in bytes (-1 if the query fails).
+int lds_bytes_of(const void* fn) {
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return -1;
+  return static_cast<int>(attr.sharedSizeBytes);
 }
 
 // Validate, pick the instance (cached per thread for an unchanged
@@ -342,7 +344,7 @@ rssm_status launch(const rssm_materialize_desc* desc, const rssm_materialize_tab
   args.ncp = ncp;
   if (verbose())
     std::fprintf(stderr, "[rssm_materialize] %s grid=%d block=%d lds=%dB L=%d B=%d H=%d checkpoints=%d\n", k->name,
-                 grid, rssm::kBlock, lds_bytes_of(desc), desc->num_layers, desc->batch, desc->num_heads, ncp);
+                 grid, rssm::kBlock, lds_bytes_of(k->fn), desc->num_layers, desc->batch, desc->num_heads, ncp);
   void* params[] = {&args};
   hipError_t e = hipLaunchKernel(k->fn, dim3(grid), dim3(rssm::kBlock), params, 0,
                                  static_cast<hipStream_t>(hip_stream));
@@ -372,9 +374,11 @@ rssm_status rssm_materialize_launch_config(const rssm_materialize_desc* desc, in
     st = materialize_grid(desc, k->fn, &g);
     if (st != RSSM_OK) return st;
   }
+  const int lds = lds_bytes_of(k->fn);
+  if (lds < 0) return fail(RSSM_ERR_HIP, "hipFuncGetAttributes failed for %s", k->name);
   *grid = g;
   *block = rssm::kBlock;
-  *lds_bytes = lds_bytes_of(desc);
+  *lds_bytes = lds;
   return RSSM_OK;
 }
 

@@ -123,6 +123,19 @@ def test_window_16_and_short_ring(dev):
     check(ri.make_problem(spec, 2200), dev)
 
 
+@pytest.mark.parametrize("state,inp,rounds", [
+    ("f32", "bf16", 0), ("f32", "f32", 0), ("bf16", "bf16", 10), ("bf16", "f32", 0), ("f16", "f16", 0),
+    ("i8", "f16", 0), ("i8", "bf16", 10), ("f8e4m3", "bf16", 10), ("f8e4m3", "f32", 0)])
+def test_window_16_dtypes(dev, state, inp, rounds):
+    """16-token windows for every state dtype (B rows of tokens 4..15 come from
+    the wavefront's LDS): prefixes U[0, 16], 4 B groups per (request, layer) so
+    each group rewrites those rows, and a ring longer than the window."""
+    spec = ri.with_(MATRIX, W=16, R=21, k_lo=0, k_hi=16, H=8, hpg=2, B=4, slots=8, ring_slots=8,
+                    state_dtype=state, input_dtype=inp, philox_rounds=rounds)
+    say("window 16", state, inp, rounds)
+    check(ri.make_problem(spec, 2600 + 10 * ri.DTYPE_CODE[state] + ri.DTYPE_CODE[inp]), dev)
+
+
 # --------------------------------------------------------------------------
 # Edge cases
 # --------------------------------------------------------------------------
@@ -246,11 +259,15 @@ def _exact_arithmetic(prob):
 
 @pytest.mark.parametrize("state", ["bf16", "f16", "i8", "f8e4m3"])
 @pytest.mark.parametrize("rounds", [0, 10])
-def test_rounding_bit_exact_on_exact_inputs(dev, state, rounds):
+@pytest.mark.parametrize("window", [8, 16])
+def test_rounding_bit_exact_on_exact_inputs(dev, state, rounds, window):
+    """Every code bit-exact where both sides hold the same fp32 values; window
+    16 takes the instances that keep B rows 4..15 in LDS."""
     import oracle
-    spec = ri.with_(MATRIX, state_dtype=state, input_dtype="bf16", philox_rounds=rounds, rand_seed=1234)
-    prob = _exact_arithmetic(ri.make_problem(spec, 2500))
-    say("bit-exact rounding", state, rounds)
+    spec = ri.with_(MATRIX, state_dtype=state, input_dtype="bf16", philox_rounds=rounds, rand_seed=1234,
+                    W=window, k_hi=window, R=window + 3, hpg=2 if window > 8 else MATRIX.hpg)
+    prob = _exact_arithmetic(ri.make_problem(spec, 2500 + window))
+    say("bit-exact rounding", state, rounds, "window", window)
     st, sc, _ = run_gpu(prob, dev)
     st_o, sc_o, ex, _ = oracle.materialize(prob, want_exact=True)
     for l in range(spec.L):
