@@ -319,27 +319,13 @@ __device__ __forceinline__ uint32_t i8_round(float t, bool stochastic, uint32_t 
   return static_cast<uint32_t>(q) & 0xFFu;
 }
 
-// e4m3 code of |t| < 464 (a row-scaled value; |t| <= 448(1 + 2^-22) in the
-// kernel), stochastic rounding, saturating at 448.  Normal range (|t| >= 2^-6):
-// e4m3 keeps the top 3 mantissa bits and the 20 dropped bits are f * 2^20, so
-// the rule is u < dropped << 12, and the carry of the increment moves into the
-// exponent field.  Below 2^-6 the grid spacing is 2^-9.
-__device__ __forceinline__ uint32_t e4m3_sr(float t, uint32_t u) {
-  const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
-  const float a = fabsf(t);
-  const uint32_t bits = __float_as_uint(a);
-  const uint32_t up_n = (u < ((bits & 0xFFFFFu) << 12)) ? 1u : 0u;
-  const uint32_t code_n = min((bits >> 20) - 960u + up_n, 0x7Eu);
-  const float s = a * 512.0f;
-  const float n = floorf(s);
-  const uint32_t code_s = static_cast<uint32_t>(n) + (sr_up(s - n, u) ? 1u : 0u);
-  return sign | (a >= 0x1p-6f ? code_n : code_s);
-}
-
-// Magnitude code (sign bit clear) of e4m3_sr for 2^-6 <= |t| < 464 only: the
-// normal-range rule without the subnormal candidate (callers check the range
-// for the whole wave first).  bits << 12 is the 20 dropped mantissa bits at
-// the top of the word; bits 30..20 are the exponent and the kept mantissa.
+// Magnitude code (sign bit clear) of stochastic e4m3 rounding for
+// 2^-6 <= |t| < 464 only (callers check the range for the whole wave first).
+// In the normal range e4m3 keeps the top 3 mantissa bits and the 20 dropped
+// bits are f * 2^20, so the rule is u < dropped << 12, and the carry of the
+// increment moves into the exponent field; the result saturates at 448.
+// bits << 12 is the 20 dropped mantissa bits at the top of the word; bits
+// 30..20 are the exponent and the kept mantissa.
 __device__ __forceinline__ uint32_t e4m3_sr_normal_mag(float t, uint32_t u) {
   const uint32_t bits = __float_as_uint(t);
   const uint32_t up = (u < (bits << 12)) ? 1u : 0u;

@@ -166,19 +166,28 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Max over the 16 lanes of an aligned lane group (one state row): swap lane
-// pairs, then pairs of pairs (quad_perm), then mirror within 8 lanes and
-// within 16 lanes.  NaN inputs are ignored, as by fmaxf.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, dpp<0x140>(v));  // row_mirror
-  return v;
+// Max over the 16 lanes of an aligned lane group (one state row) of values
+// that are >= +0 and not NaN: swap lane pairs, then pairs of pairs
+// (quad_perm), then mirror within 8 lanes and within 16 lanes.  The bit
+// patterns of such values order as unsigned integers, so each step is one
+// integer max with the lane exchange folded in (a float max would also
+// quiet the moved value first).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float row16_max_nonneg(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = max(u, dpp_u32<0xB1>(u));   // quad_perm [1,0,3,2]
+  u = max(u, dpp_u32<0x4E>(u));   // quad_perm [2,3,0,1]
+  u = max(u, dpp_u32<0x141>(u));  // row_half_mirror
+  u = max(u, dpp_u32<0x140>(u));  // row_mirror
+  return __uint_as_float(u);
 }
 
 // Sum over the 16 lanes of an aligned lane group, every lane receiving the
-// total (the same exchange pattern as row16_max).
+// total (the same exchange pattern as row16_max_nonneg).
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
@@ -210,10 +219,12 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
     // both correctly rounded fp32 quotients (row_quant).  An all-zero row (or
     // one whose inverse overflows) stores scale 0 and zero codes.
     constexpr int qmax = (ST == kI8) ? 127 : 448;
+    // The lane's max starts at +0 and fmaxf ignores NaN elements, so m is
+    // >= +0 and never NaN.
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(acc[i]));
-    m = row16_max(m);
+    m = row16_max_nonneg(m);
     float inv;
     const bool ok = row_quant<qmax>(m, row_scale, inv);
     float t[8];
@@ -242,22 +253,18 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
       out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
       out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
     } else {
-      // |t| <= 448(1 + 2^-22) for every finite element of a valid row.  NaN
-      // elements (ignored by the row max) take the general path.
-      if (any_nan()) {
+      // |t| <= 448(1 + 2^-22) for every finite element of a valid row.
+      if constexpr (SR) {
+        // NaN elements (ignored by the row max) and elements below 2^-6 (where
+        // the subnormal grid applies) are rare: one compare finds both, and a
+        // wavefront holding any takes the general rule for all its elements.
         uint32_t code[8];
+        bool rare = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) code[i] = e4m3_round(t[i], SR, u[i]);
-        out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
-        out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
-      } else if constexpr (SR) {
-        uint32_t code[8];
-        bool has_sub = false;
+        for (int i = 0; i < 8; ++i) rare |= !(fabsf(t[i]) >= 0x1p-6f);
+        if (__builtin_expect(__ballot(rare) != 0, 0)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) has_sub |= (fabsf(t[i]) < 0x1p-6f);
-        if (__ballot(has_sub) != 0) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) code[i] = e4m3_sr(t[i], u[i]);
+          for (int i = 0; i < 8; ++i) code[i] = e4m3_round(t[i], true, u[i]);
           out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
           out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
         } else {
@@ -273,6 +280,13 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
                        pack_low_bytes(code[4 * w], code[4 * w + 1], code[4 * w + 2], code[4 * w + 3]);
           }
         }
+      } else if (any_nan()) {
+        // NaN elements (ignored by the row max) take the general rule.
+        uint32_t code[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[i] = e4m3_round(t[i], false, u[i]);
+        out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
+        out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
       } else {
         // Hardware nearest-even conversion: equal to e4m3_round for |t| < 464
         // (checked on gfx950), which covers every finite row-scaled value.
