@@ -319,17 +319,18 @@ __device__ __forceinline__ uint32_t i8_round(float t, bool stochastic, uint32_t 
   return static_cast<uint32_t>(q) & 0xFFu;
 }
 
-// Magnitude code (sign bit clear) of stochastic e4m3 rounding for
-// 2^-6 <= |t| < 464 only (callers check the range for the whole wave first).
-// In the normal range e4m3 keeps the top 3 mantissa bits and the 20 dropped
-// bits are f * 2^20, so the rule is u < dropped << 12, and the carry of the
-// increment moves into the exponent field; the result saturates at 448.
-// bits << 12 is the 20 dropped mantissa bits at the top of the word; bits
-// 30..20 are the exponent and the kept mantissa.
-__device__ __forceinline__ uint32_t e4m3_sr_normal_mag(float t, uint32_t u) {
-  const uint32_t bits = __float_as_uint(t);
-  const uint32_t up = (u < (bits << 12)) ? 1u : 0u;
-  return min(((bits >> 20) & 0x7FFu) - 960u + up, 0x7Eu);
+// Magnitude code of stochastic e4m3 rounding for a = |t| with
+// 2^-6 <= a < 464 only (callers check the range for the whole wave first);
+// abits are the bits of a (sign clear).  In the normal range e4m3 keeps the
+// top 3 mantissa bits and the 20 dropped bits d are f * 2^20, so the rule
+// rounds up iff u < d * 2^12, i.e. iff (u >> 12) < d, i.e. iff adding
+// 0xFFFFF - (u >> 12) = (u >> 12) ^ 0xFFFFF to the bits carries into bit 20,
+// the lowest kept bit.  Bits 30..20 (exponent and kept mantissa) then hold
+// the rounded value; subtracting 960 << 20 rebiases the exponent (bias 127
+// to bias 7), and the result saturates at 448 (code 0x7E).
+__device__ __forceinline__ uint32_t e4m3_sr_normal_mag(uint32_t abits, uint32_t u) {
+  const uint32_t v = abits + ((u >> 12) ^ 0xFFFFFu) - (960u << 20);
+  return min(v >> 20, 0x7Eu);
 }
 
 // General e4m3 rounding (any input): nearest-even or stochastic, saturating;

@@ -258,24 +258,29 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
         // NaN elements (ignored by the row max) and elements below 2^-6 (where
         // the subnormal grid applies) are rare: one compare finds both, and a
         // wavefront holding any takes the general rule for all its elements.
+        // The common path works on |t| = |acc| * inv and takes the sign bits
+        // from acc (inv > 0): bit 7 of byte 3 of each fp32 value is its sign,
+        // which goes to bit 7 of its code byte.
         uint32_t code[8];
+        float ta[8];
         bool rare = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rare |= !(fabsf(t[i]) >= 0x1p-6f);
+        for (int i = 0; i < 8; ++i) {
+          ta[i] = fabsf(acc[i]) * inv;
+          rare |= !(ta[i] >= 0x1p-6f);
+        }
         if (__builtin_expect(__ballot(rare) != 0, 0)) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) code[i] = e4m3_round(t[i], true, u[i]);
           out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
           out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
         } else {
-          // Magnitude codes, then the sign bits: bit 7 of byte 3 of each fp32
-          // value is its sign, which goes to bit 7 of its code byte.
 #pragma unroll
-          for (int i = 0; i < 8; ++i) code[i] = e4m3_sr_normal_mag(t[i], u[i]);
+          for (int i = 0; i < 8; ++i) code[i] = e4m3_sr_normal_mag(__float_as_uint(ta[i]), u[i]);
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
-            const uint32_t sg = pack_high_bytes(__float_as_uint(t[4 * w]), __float_as_uint(t[4 * w + 1]),
-                                                __float_as_uint(t[4 * w + 2]), __float_as_uint(t[4 * w + 3]));
+            const uint32_t sg = pack_high_bytes(__float_as_uint(acc[4 * w]), __float_as_uint(acc[4 * w + 1]),
+                                                __float_as_uint(acc[4 * w + 2]), __float_as_uint(acc[4 * w + 3]));
             out.w[w] = (sg & 0x80808080u) |
                        pack_low_bytes(code[4 * w], code[4 * w + 1], code[4 * w + 2], code[4 * w + 3]);
           }
