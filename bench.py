@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,10 +40,19 @@ def say(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed (the kernel
+    sources hold no string literals), so that comment edits keep the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash() -> str:
+    """Hash of the materialize kernel's code (comments and layout ignored)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, p)).read()).encode())
     return h.hexdigest()[:16]
 
 

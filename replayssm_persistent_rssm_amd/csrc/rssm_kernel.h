@@ -23,7 +23,8 @@
 //  * Decay weights come from a wavefront-level suffix-product scan over the k
 //    per-token decays a_j = exp(dt_j A_h) held one per lane.
 //  * w_j * x_j is staged per wavefront in LDS ([row][token], fp32); each lane
-//    owns 8 consecutive columns, keeps B_j for those columns in registers, and
+//    owns 8 columns, keeps B_j for those columns in registers (16-token
+//    windows: tokens 0..3 in registers, 4..15 in the wavefront's LDS), and
 //    streams its rows of the tile through registers with 16-byte loads (8-byte
 //    for one-byte state), folding k multiply-adds per element.  No MFMA: the
 //    path moves ~4 bytes per 2k+1 flops and is bound by HBM.
