@@ -446,8 +446,17 @@ def gdn_workload(dev, stream, steps):
            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "us_per_request": round(ms * 1e3 / max(live, 1), 3)}
+    # every request null: the work discovery alone (nothing is written)
+    null_idx = torch.full((spec.B,), spec.null_block_id, dtype=torch.int32, device=dev)
+    null_call = rp.GdnCommitCall(dp.state, dp.rawv, dp.rawk, dp.g, dp.beta, null_idx, meta[1],
+                                 track_state_indices=meta[2], track_steps=meta[3],
+                                 null_block_id=spec.null_block_id)
+    for _ in range(20):
+        null_call()
+    torch.cuda.synchronize()
+    out["all_null_us"] = round(timed_calls(null_call, 1000, stream) * 1e3, 3)
     say(f"gdn_commit: {out}")
-    del call, dp, meta
+    del call, null_call, dp, meta
     torch.cuda.empty_cache()
     return out
 

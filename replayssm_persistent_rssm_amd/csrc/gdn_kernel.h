@@ -113,8 +113,37 @@ __global__ void __launch_bounds__(kBlock, (WPS > 0 ? WPS : kGdnWavesPerSimd<TMAX
 
   int cur_b = -1, s = 0, n = 0, ts = -1, step = -1;
   bool live = false;
+  // Tiles dealt round-robin, several per wavefront: the wavefront first tests
+  // the liveness of its next 64 tiles at once (one per lane: the request's
+  // slot above null_block_id and a positive accepted count) and walks only the
+  // live ones, so skipped requests cost no round trips of their own (a call
+  // whose requests are all null is one near-empty launch).
+  const bool filt = DEAL == 1 && items > tw;
+  int64_t qb = 0;       // position in this wavefront's tile sequence of lane 0 of the batch
+  uint64_t livem = 0;   // live tiles of the batch not yet taken
 
-  while (it < end) {
+  for (;;) {
+    if (filt) {
+      while (livem == 0) {
+        if (gw + qb * tw >= items) break;
+        const int64_t tj = gw + (qb + lane) * tw;
+        bool lv = false;
+        if (tj < items) {
+          const int bj = static_cast<int>(tj / per_req);
+          const int sj = gload(a.state_indices + bj);
+          const int nj = gload(a.accept_lens + bj);
+          lv = sj > a.null_block_id && sj < a.slots && nj > 0;
+        }
+        livem = __ballot(lv);
+        if (livem == 0) qb += 64;
+      }
+      if (livem == 0) break;
+      it = gw + (qb + __builtin_ctzll(livem)) * tw;
+      livem &= livem - 1;
+      if (livem == 0) qb += 64;
+    } else if (it >= end) {
+      break;
+    }
     const int b = static_cast<int>(it / per_req);
     if (b != cur_b) {
       // Request metadata, read when the request changes.

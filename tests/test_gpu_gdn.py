@@ -117,6 +117,24 @@ def test_grid_invariance(dev):
         assert np.array_equal(run(prob, dev, max_workgroups=g).view(np.uint32), ref.view(np.uint32)), g
 
 
+@pytest.mark.parametrize("null_frac", [0.5, 1.0])
+def test_null_requests_many_tiles_per_wave(dev, null_frac):
+    """Null slots and zero accepted counts mixed with live requests (or every
+    request null) on grids of 1-2 workgroups: each wavefront deals up to 192
+    tiles, so it tests their liveness in several batches of 64 and skips the
+    dead ones; the default grid as well."""
+    spec = ri.with_(ri.GDN_CONFIGS["gdn_small"], B=24, L=4, HV=8, H=4, slots=56, null_frac=null_frac,
+                    zero_frac=0.2 if null_frac < 1 else 0.0)
+    prob = ri.make_gdn_problem(spec, 75)
+    for g in (1, 2, 0):
+        say("null_frac", null_frac, "grid", g)
+        got = run(prob, dev, max_workgroups=g)
+        if null_frac == 1.0:
+            assert np.array_equal(got.view(np.uint32), prob.state.view(np.uint32)), "an all-null call wrote"
+        else:
+            assert check(prob, got, f"null_frac {null_frac} grid {g}").any()
+
+
 def test_full_size_sampled(dev):
     """gdn_large at full size, in the launch the benchmark times: sampled
     tiles against the oracle (the states are copied before the in-place
