@@ -726,9 +726,10 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
         }
 
         // Stage w_j * x_j[r] into this wave's LDS as [row][token].  Tokens
-        // k..ceil4(k)-1 pad the last block of four with -0.0: with B_j = +0
-        // their fused multiply-add adds -0, which leaves every accumulator
-        // unchanged (including the sign of a zero).
+        // k..ceil4(k)-1 pad the last block of four (the single-checkpoint fold
+        // takes blocks of two, the multi-checkpoint fold blocks of four) with
+        // -0.0: with B_j = +0 their fused multiply-add adds -0, which leaves
+        // every accumulator unchanged (including the sign of a zero).
         const int k4 = (k + 3) & ~3;
         wave_lds_fence();
 #pragma unroll
@@ -778,15 +779,13 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[c] *= d0;
 #pragma unroll
-                for (int jb = 0; jb < KMAX / 4; ++jb) {
-                  if (jb * 4 < k) {
-                    const float4 w4 = *reinterpret_cast<const float4*>(wrow + jb * 4);
+                for (int jb = 0; jb < KMAX / 2; ++jb) {
+                  if (jb * 2 < k) {
+                    const float2 w2 = *reinterpret_cast<const float2*>(wrow + jb * 2);
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
-                      acc[c] = fmaf(w4.x, Bat(jb * 4 + 0, c), acc[c]);
-                      acc[c] = fmaf(w4.y, Bat(jb * 4 + 1, c), acc[c]);
-                      acc[c] = fmaf(w4.z, Bat(jb * 4 + 2, c), acc[c]);
-                      acc[c] = fmaf(w4.w, Bat(jb * 4 + 3, c), acc[c]);
+                      acc[c] = fmaf(w2.x, Bat(jb * 2 + 0, c), acc[c]);
+                      acc[c] = fmaf(w2.y, Bat(jb * 2 + 1, c), acc[c]);
                     }
                   }
                 }
