@@ -242,16 +242,19 @@ rssm_status grid_for(const void* fn, int* grid_out) {
 }
 
 // Default grid of the materialize kernels (the work loop is persistent either
-// way).  One-byte state: four times the resident capacity, which ran 5-6%
-// faster than one workgroup per resident slot on the int8 and e4m3 workloads
-// on MI355X (their requests differ more in cost).  Other state: the resident
-// capacity; four times it was within 0.5% on bf16 but raised the empty call's
-// kernel time from 2.5 to 3.5 us.
+// way).  A larger grid lets the hardware hand out workgroups as others
+// finish, which balances requests of different cost; every workgroup also
+// adds about 0.4 us per thousand to a call with nothing to do.  One-byte
+// state (its requests differ more in cost): eight times the resident
+// capacity, which on MI355X ran 2% (int8) and 6% (e4m3 + Philox) faster than
+// four times and 10-15% faster than one, for an empty call of about 5 us
+// under graph replay.  Other state: the resident capacity; eight times it was
+// 0.8% faster on bf16 but raised the empty call from 1.7 to 4.4 us.
 rssm_status materialize_grid(const rssm_materialize_desc* d, const void* fn, int* grid_out) {
   int resident = 0;
   rssm_status st = grid_for(fn, &resident);
   if (st != RSSM_OK) return st;
-  *grid_out = one_byte(d->state_dtype) ? 4 * resident : resident;
+  *grid_out = one_byte(d->state_dtype) ? 8 * resident : resident;
   return RSSM_OK;
 }
 
