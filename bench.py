@@ -182,7 +182,7 @@ def main():
         rp.use_contiguous_allocator()
     dev = torch.device("cuda:0")
     if args.only_gdn:
-        print(json.dumps({"gdn_commit": gdn_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
+        print(json.dumps({"gdn_commit": gdn_workload(dev, torch.cuda.current_stream(), args.steps, with_null=False)}), flush=True)
         return
     if args.only_ssu:
         print(json.dumps({"ssu_decode": ssu_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
@@ -415,7 +415,7 @@ def checkpoint_workload(dp, tabs, spec, stream, steps):
     return out
 
 
-def gdn_workload(dev, stream, steps):
+def gdn_workload(dev, stream, steps, with_null: bool = True):
     """The gated-delta-rule commit on gdn_large: 48 layers, 256 requests (a
     sixteenth with a null slot, a sixteenth accepting nothing, the rest
     accepting U[0, 8] tokens), 32 value heads over 16 key heads, fp32 128x128
@@ -446,7 +446,13 @@ def gdn_workload(dev, stream, steps):
            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "us_per_request": round(ms * 1e3 / max(live, 1), 3)}
-    # every request null: the work discovery alone (nothing is written)
+    # every request null: the work discovery alone (nothing is written); left
+    # out in the profile mode, whose trace then holds only the full calls
+    if not with_null:
+        say(f"gdn_commit: {out}")
+        del call, dp, meta
+        torch.cuda.empty_cache()
+        return out
     null_idx = torch.full((spec.B,), spec.null_block_id, dtype=torch.int32, device=dev)
     null_call = rp.GdnCommitCall(dp.state, dp.rawv, dp.rawk, dp.g, dp.beta, null_idx, meta[1],
                                  track_state_indices=meta[2], track_steps=meta[3],
