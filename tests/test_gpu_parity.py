@@ -336,7 +336,10 @@ def test_row_scales_correctly_rounded(dev):
     """The one-byte encode's row scale m/qmax and inverse qmax/m equal IEEE
     fp32 division (numpy float32) bit for bit: every mantissa at exponents on
     both sides of the short sequences' range [2^-100, 2^100] and at the ends
-    of the normal range, the first 2^20 subnormals, and special values."""
+    of the normal range, the first 2^20 subnormals, and special values.
+    Inside the range the sequences only scale by powers of two with m (no
+    operand nears the subnormal or overflow range), so every mantissa at one
+    exponent stands for the whole range."""
     import torch
     from replayssm_persistent_rssm_amd import rssm_debug_row_scales
     mant = np.arange(1 << 23, dtype=np.uint32)
