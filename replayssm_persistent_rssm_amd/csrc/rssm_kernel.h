@@ -778,9 +778,15 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
                 const float d0 = Q ? cur_sc * Dseg[0] : Dseg[0];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[c] *= d0;
+                // An opaque scalar copy of k per pass: each block test is then
+                // one scalar compare and branch (shared with other uses of
+                // j < k, the tests become lane masks whose branches cost two
+                // vector instructions each).
+                int kk = k;
+                asm volatile("" : "+s"(kk));
 #pragma unroll
                 for (int jb = 0; jb < KMAX / 2; ++jb) {
-                  if (jb * 2 < k) {
+                  if (jb * 2 < kk) {
                     const float2 w2 = *reinterpret_cast<const float2*>(wrow + jb * 2);
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
