@@ -371,7 +371,7 @@ def test_row_scales_correctly_rounded(dev):
 # --------------------------------------------------------------------------
 # Full-size workloads, sampled (launch configuration of the benchmark)
 # --------------------------------------------------------------------------
-def _sampled_full_size(dev, name, n_active, seed, n_samples=24):
+def _sampled_full_size(dev, name, n_active, seed, n_samples=24, all_pad_after=False):
     import torch
     import oracle
     import parity
@@ -430,6 +430,16 @@ def _sampled_full_size(dev, name, n_active, seed, n_samples=24):
         for l in (0, spec.L - 1):
             t = dp.state[l][free_dst[:4]].view(torch.uint8)
             assert bool((t == 0xA5).all().item()), "an unlisted destination slot was written"
+    if all_pad_after:
+        # the same listed requests with every source slot the pad slot: the
+        # launch (the benchmark's all-pad call) must leave every pool byte as is
+        say("full size", name, "all listed, every source the pad slot")
+        pad_src = torch.full((spec.L, spec.B), spec.pad_slot_id, dtype=torch.int32, device=dev)
+        sums = [int(t.view(torch.int32).to(torch.int64).sum().item()) for t in dp.state]
+        hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "src_slots": pad_src}))()
+        torch.cuda.synchronize()
+        assert sums == [int(t.view(torch.int32).to(torch.int64).sum().item()) for t in dp.state], \
+            "an all-pad call wrote"
     del dp, tabs
     torch.cuda.empty_cache()
     return listed
@@ -437,7 +447,7 @@ def _sampled_full_size(dev, name, n_active, seed, n_samples=24):
 
 @pytest.mark.parametrize("n_active", [256, 16])
 def test_full_size_large_bf16_sampled(dev, n_active):
-    _sampled_full_size(dev, "large_bf16", n_active, 1000 + 2 * 10 + n_active % 7)
+    _sampled_full_size(dev, "large_bf16", n_active, 1000 + 2 * 10 + n_active % 7, all_pad_after=n_active == 256)
 
 
 def test_full_size_large_i8_sampled(dev):
