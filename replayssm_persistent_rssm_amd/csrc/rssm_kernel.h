@@ -335,16 +335,25 @@ __device__ __forceinline__ int ring_entry(int r0, int j, int R) {
 // gained 14%.  For int8 with 8-token windows, 4 rows in LDS ran 5% slower.
 template <int KMAX> constexpr int kBRegs = (KMAX > 8) ? 4 : KMAX;
 
+// int8 state, fp16 x/B, windows of up to 8, one checkpoint: B rows held as
+// packed fp16 pairs and multiplied with v_fma_mix_f32, which leaves room for
+// 5 waves per SIMD (4.3% faster than fp32 rows at 4 waves on MI355X; at 4
+// waves the packed rows alone ran 1% slower).
+template <int ST, int IT, int KMAX, int NCK>
+constexpr bool kMixB = (ST == kI8 && IT == kF16 && KMAX <= 8 && NCK == 1);
+
 // Resident wavefronts per SIMD the register budget is sized for.
 // e4m3 state adds software decode/encode on top of the row scales: its
 // 8-token instances get a 3-wave budget (168 registers) so they do not spill.
-// int8 keeps 4 waves: it runs ~11% faster than with 3 waves on MI355X,
-// although the compiler then spills a few registers outside the fold.
+// int8 keeps 4 waves (5 with packed fp16 B rows, above): it runs ~11% faster
+// than with 3 waves on MI355X, although the compiler then spills a few
+// registers outside the fold.
 // 16-token instances get 4 waves, except with fp32 x/B (16 raw 32-byte B
 // chunks are held while a group's rows load) and the multi-checkpoint
 // instances (segment bookkeeping): 3 waves, where they do not spill.
 template <int KMAX, int ST, int IT, int NCK>
-constexpr int kWavesPerSimd = (KMAX > 8) ? ((IT == kF32 || NCK > 1) ? 3 : 4) : ((ST == kF8) ? 3 : 4);
+constexpr int kWavesPerSimd = (KMAX > 8) ? ((IT == kF32 || NCK > 1) ? 3 : 4)
+                                         : ((ST == kF8) ? 3 : (kMixB<ST, IT, KMAX, NCK> ? 5 : 4));
 
 // Knobs of the state stream.  The library's instances use the defaults; the
 // alternatives exist so that streaming patterns can be compared on hardware.
@@ -635,7 +644,14 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
       // the lanes of row 0 of each pass).  All KMAX rows are requested at once
       // (tokens past k re-read entry r0 and are then zeroed), so the group
       // costs one round trip, not k.
-      float Bv[KREG][8];
+      // int8 state with fp16 x/B and windows of up to 8 (single checkpoint):
+      // the register rows stay packed fp16 pairs (word q holds columns 2q,
+      // 2q+1) and the fold multiplies them with v_fma_mix_f32 (fp16 operand
+      // converted exactly, one fp32 rounding: the same result as fmaf on the
+      // decoded value).  That frees 32 registers for a fifth wave per SIMD.
+      constexpr bool kMix = kMixB<ST, IT, KMAX, NCK>;
+      float Bv[kMix ? 1 : KREG][8];
+      uint32_t Bh[kMix ? KREG : 1][4];
       {
         Chunk<IT> braw[KMAX];
 #pragma unroll
@@ -651,8 +667,13 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[q] = (j < k) ? v[q] : 0.0f;
           if (j < KREG) {
+            if constexpr (kMix) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) Bv[j < KREG ? j : 0][q] = v[q];
+              for (int q = 0; q < 4; ++q) Bh[j < KREG ? j : 0][q] = (j < k) ? braw[j].w[q] : 0u;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) Bv[j < KREG ? j : 0][q] = v[q];
+            }
           } else if (rr == 0) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) bl[(j >= KREG ? j - KREG : 0) * DSTATE + cc * 8 + q] = v[q];
@@ -661,7 +682,13 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
       }
       // B_j[c] of this lane's columns (j and c are compile-time after unrolling).
       auto Bat = [&](int j, int c) -> float {
-        return j < KREG ? Bv[j < KREG ? j : 0][c] : bl[(j >= KREG ? j - KREG : 0) * DSTATE + cc * 8 + c];
+        if (j >= KREG) return bl[(j >= KREG ? j - KREG : 0) * DSTATE + cc * 8 + c];
+        if constexpr (kMix) {
+          const uint32_t w = Bh[j < KREG ? j : 0][c >> 1];
+          return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>((c & 1) ? (w >> 16) : (w & 0xFFFFu))));
+        } else {
+          return Bv[j < KREG ? j : 0][c];
+        }
       };
       const int hb = max(h0, g * a.hpg);
       const int he = min(h1, (g + 1) * a.hpg);
@@ -784,6 +811,15 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
                 // vector instructions each).
                 int kk = k;
                 asm volatile("" : "+s"(kk));
+                // Packed fp16 rows: an opaque copy per pass keeps their
+                // conversion inside v_fma_mix_f32 (hoisted out of the pass
+                // loop, the converted rows would take the registers back).
+                if constexpr (kMix) {
+#pragma unroll
+                  for (int j = 0; j < KREG; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(Bh[j][q]));
+                }
 #pragma unroll
                 for (int jb = 0; jb < KMAX / 2; ++jb) {
                   if (jb * 2 < kk) {

@@ -259,15 +259,16 @@ def _exact_arithmetic(prob):
 
 @pytest.mark.parametrize("state", ["bf16", "f16", "i8", "f8e4m3"])
 @pytest.mark.parametrize("rounds", [0, 10])
-@pytest.mark.parametrize("window", [8, 16])
-def test_rounding_bit_exact_on_exact_inputs(dev, state, rounds, window):
+@pytest.mark.parametrize("window,inp", [(8, "bf16"), (16, "bf16"), (8, "f16")])
+def test_rounding_bit_exact_on_exact_inputs(dev, state, rounds, window, inp):
     """Every code bit-exact where both sides hold the same fp32 values; window
-    16 takes the instances that keep B rows 4..15 in LDS."""
+    16 takes the instances that keep B rows 4..15 in LDS, fp16 inputs with
+    int8 state the instance that multiplies packed fp16 B rows."""
     import oracle
-    spec = ri.with_(MATRIX, state_dtype=state, input_dtype="bf16", philox_rounds=rounds, rand_seed=1234,
+    spec = ri.with_(MATRIX, state_dtype=state, input_dtype=inp, philox_rounds=rounds, rand_seed=1234,
                     W=window, k_hi=window, R=window + 3, hpg=2 if window > 8 else MATRIX.hpg)
     prob = _exact_arithmetic(ri.make_problem(spec, 2500 + window))
-    say("bit-exact rounding", state, rounds, "window", window)
+    say("bit-exact rounding", state, rounds, "window", window, "input", inp)
     st, sc, _ = run_gpu(prob, dev)
     st_o, sc_o, ex, _ = oracle.materialize(prob, want_exact=True)
     for l in range(spec.L):
