@@ -26,8 +26,8 @@ def rocrand_ref(tmp_path_factory):
     subprocess.check_call([cxx, "-O1", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I" + ROCRAND_INC,
                            os.path.join(HERE, "pins", "rocrand_philox_ref.cpp"), "-o", exe])
 
-    def run(rows):
-        text = "".join("%08x %08x %08x %08x %08x %08x\n" % tuple(int(v) for v in r) for r in rows)
+    def run(rows, rounds=10):
+        text = "".join("%08x %08x %08x %08x %08x %08x %d\n" % (tuple(int(v) for v in r) + (rounds,)) for r in rows)
         out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
         return np.array([[int(w, 16) for w in line.split()] for line in out.strip().splitlines()], np.uint64)
     return run
@@ -41,6 +41,28 @@ def test_philox10_matches_rocrand(orc, rocrand_ref):
     ref = rocrand_ref(rows)
     got = np.array([orc.philox4x32(r[:4], r[4:], 10) for r in rows], np.uint64)
     np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("rounds", [1, 2, 3, 7, 12])
+def test_philox_other_round_counts_match_rocrand_rounds(orc, rocrand_ref, rounds):
+    """Round counts other than 10: rocRAND's own single round and key bump,
+    applied `rounds` times (the published R-round construction)."""
+    rng = np.random.default_rng(100 + rounds)
+    rows = rng.integers(0, 2**32, size=(200, 6), dtype=np.uint64)
+    rows = np.vstack([rows, [[0] * 6, [0xFFFFFFFF] * 6, [31, 127, 255, 47, 1234, 0]]])
+    ref = rocrand_ref(rows, rounds)
+    got = np.array([orc.philox4x32(r[:4], r[4:], rounds) for r in rows], np.uint64)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_rocrand_round_composition_equals_its_ten_round_block(rocrand_ref):
+    """The pin program's composition of rocRAND's single round and key bump,
+    run for 10 rounds, reproduces rocRAND's shipped ten-round block: the
+    composition used for the other round counts is the generator's own."""
+    rng = np.random.default_rng(99)
+    rows = rng.integers(0, 2**32, size=(100, 6), dtype=np.uint64)
+    np.testing.assert_array_equal(rocrand_ref(rows, -10), rocrand_ref(rows, 10))
+    assert not np.array_equal(rocrand_ref(rows, 11), rocrand_ref(rows, 10))
 
 
 def test_philox_zero_rounds_is_identity(orc):

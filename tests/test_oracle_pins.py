@@ -171,14 +171,42 @@ def test_ring_wrap_equals_unrolled_ring(orc):
     assert np.array_equal(ex[0][dslot], ex2[0][dslot])
 
 
+def decode_independent(dtype, codes):
+    """Stored codes as fp64 values without the oracle: numpy for fp32/int8,
+    torch's CPU casts for bf16, fp16 and OCP e4m3fn."""
+    import torch
+    codes = np.ascontiguousarray(codes)
+    if dtype == "f32":
+        return codes.view(np.float32).astype(np.float64)
+    if dtype == "i8":
+        return codes.view(np.int8).astype(np.float64)
+    tdt = {"bf16": (torch.int16, torch.bfloat16), "f16": (torch.int16, torch.float16),
+           "f8e4m3": (torch.uint8, torch.float8_e4m3fn)}[dtype]
+    raw = torch.from_numpy(codes.view(np.int16 if tdt[0] == torch.int16 else np.uint8).copy())
+    return raw.view(tdt[1]).to(torch.float64).numpy()
+
+
+def spread_row_scales(prob, seed):
+    """Replace every row scale of every slot (sources, destinations, gaps) by
+    an independent power of two in [2^-8, 2^8] times U[1, 2): a scale read
+    from the wrong row, the wrong slot, or not applied at all changes the
+    dequantized state by a large factor."""
+    rng = np.random.default_rng(seed)
+    for sc in prob.scale:
+        sc[:] = (np.exp2(rng.integers(-8, 9, size=sc.shape)) * rng.uniform(1.0, 2.0, size=sc.shape)).astype(np.float32)
+
+
 def _unrolled(prob, l, b, s, h):
-    """D*S0 + sum_j w_j x_j B_j^T in fp64 (closed form of the recurrence)."""
-    import oracle
+    """D*S0 + sum_j w_j x_j B_j^T in fp64 (closed form of the recurrence).
+    One-byte sources dequantize as code times the source slot's row scale
+    (the materialize page's state_scale_ptrs hold the quantized state's
+    scales; the pull-request page's change table reads them as the decode
+    scale input), decoded here without the oracle."""
     spec = prob.spec
     k, r0 = int(prob.meta.prefix[b]), int(prob.meta.ring_start[b])
     x, B, dt = ring_views(prob, l, s)
     n = spec.dim * spec.dstate
-    S0 = oracle.decode(spec.state_dtype, prob.state[l][s, h * n:(h + 1) * n]).reshape(spec.dim, spec.dstate)
+    S0 = decode_independent(spec.state_dtype, prob.state[l][s, h * n:(h + 1) * n]).reshape(spec.dim, spec.dstate)
     if prob.scale:
         S0 = S0 * prob.scale[l][s, h * spec.dim:(h + 1) * spec.dim].astype(np.float64)[:, None]
     A = float(prob.A[l][h])
@@ -193,10 +221,13 @@ def _unrolled(prob, l, b, s, h):
     return out
 
 
+@pytest.mark.parametrize("dtype", ["f32", "i8", "f8e4m3"])
 @pytest.mark.parametrize("k", [1, 3, 8])
-def test_unrolled_sum_and_single_step(orc, k):
-    spec = ri.with_(SMALL, prefix=[k] * 4)
+def test_unrolled_sum_and_single_step(orc, k, dtype):
+    spec = ri.with_(SMALL, prefix=[k] * 4, state_dtype=dtype, input_dtype="f32" if dtype == "f32" else "bf16")
     prob = ri.make_problem(spec, 27 + k)
+    if prob.scale:
+        spread_row_scales(prob, 270 + k)
     _, _, ex, _ = orc.materialize(prob, want_exact=True)
     n = spec.dim * spec.dstate
     for l, b, s, d in written_pairs(prob):
@@ -240,6 +271,34 @@ def test_closed_form_pure_decay_when_x_zero(orc):
             tot = sum(dt[(r0 + j) % spec.R, h] for j in range(k))
             ref = np.exp(float(prob.A[l][h]) * tot) * prob.state[l][s, h * n:(h + 1) * n].astype(np.float64)
             np.testing.assert_allclose(ex[l][d, h * n:(h + 1) * n], ref, rtol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["i8", "f8e4m3"])
+def test_one_byte_source_pure_decay(orc, dtype):
+    """x = 0 on a one-byte source: every element of the result is
+    exp(A_h * sum_j dt_j) * code[r, c] * scale_src[r], with codes decoded by
+    numpy / torch and row scales spread over 2^-8 .. 2^9.  A scale taken by
+    column, from the destination slot, or left out fails here."""
+    spec = ri.with_(SMALL, state_dtype=dtype, input_dtype="bf16", prefix=[4, 7, 2, 8])
+    prob = ri.make_problem(spec, 35)
+    spread_row_scales(prob, 350)
+    for l in range(spec.L):
+        prob.x[l][:] = 0
+    _, _, ex, _ = orc.materialize(prob, want_exact=True)
+    n = spec.dim * spec.dstate
+    checked = 0
+    for l, b, s, d in written_pairs(prob):
+        _, _, dt = ring_views(prob, l, s)
+        k, r0 = int(prob.meta.prefix[b]), int(prob.meta.ring_start[b])
+        assert k > 0
+        for h in range(spec.H):
+            tot = sum(dt[(r0 + j) % spec.R, h] for j in range(k))
+            codes = decode_independent(dtype, prob.state[l][s, h * n:(h + 1) * n]).reshape(spec.dim, spec.dstate)
+            rows = prob.scale[l][s, h * spec.dim:(h + 1) * spec.dim].astype(np.float64)
+            ref = np.exp(float(prob.A[l][h]) * tot) * codes * rows[:, None]
+            np.testing.assert_allclose(ex[l][d, h * n:(h + 1) * n].reshape(spec.dim, spec.dstate), ref, rtol=1e-12)
+            checked += 1
+    assert checked > 0
 
 
 def test_closed_form_geometric_series(orc):
