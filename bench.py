@@ -34,6 +34,24 @@ SEED = 1002
 SEEDS = {"large_bf16": 1002, "large_i8": 1003, "large_f8sr": 1004}
 KERNEL_SOURCES = ["replayssm_persistent_rssm_amd/csrc/rssm_kernel.h",
                   "replayssm_persistent_rssm_amd/csrc/rssm_device.h"]
+# Kernel sources behind each counter workload (their code hash is recorded
+# with the counters, and traffic is reported only while it matches).
+COUNTER_SOURCES = {
+    "large_bf16": KERNEL_SOURCES, "large_i8": KERNEL_SOURCES, "large_f8sr": KERNEL_SOURCES,
+    "checkpoints": KERNEL_SOURCES,
+    "gdn_large": ["replayssm_persistent_rssm_amd/csrc/gdn_kernel.h", "replayssm_persistent_rssm_amd/csrc/rssm_device.h"],
+    "ssu_large": ["replayssm_persistent_rssm_amd/csrc/ssu_kernel.h", "replayssm_persistent_rssm_amd/csrc/rssm_device.h"],
+}
+# rocprofv3 kernel-name fragment and counter-summary file of each counter workload
+COUNTER_KERNEL = {"large_bf16": "materialize_kernel", "large_i8": "materialize_kernel",
+                  "large_f8sr": "materialize_kernel", "checkpoints": "materialize_kernel",
+                  "gdn_large": "gdn_commit_kernel", "ssu_large": "ssu_decode_kernel"}
+COUNTER_FILE = {"large_bf16": "materialize_large_bf16_counters.txt",
+                "large_i8": "materialize_large_i8_counters.txt",
+                "large_f8sr": "materialize_large_f8sr_counters.txt",
+                "checkpoints": "materialize_checkpoints_large_bf16_counters.txt",
+                "gdn_large": "gdn_commit_gdn_large_counters.txt",
+                "ssu_large": "ssu_decode_ssu_large_counters.txt"}
 
 
 def say(*a):
@@ -48,18 +66,19 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_hash() -> str:
-    """Hash of the materialize kernel's code (comments and layout ignored)."""
+def kernel_hash(sources=None) -> str:
+    """Hash of a kernel's code (comments and layout ignored); default: the
+    materialize kernel."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (sources or KERNEL_SOURCES):
         h.update(_code_only(open(os.path.join(ROOT, p)).read()).encode())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(bytes_alg: int):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "materialize_large_bf16_counters.txt")
+def counter_values(workload: str):
+    """Key/value lines of the committed counter summary of a workload, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", COUNTER_FILE[workload])
     if not os.path.exists(path):
         return None
     vals = {}
@@ -67,10 +86,27 @@ def traffic_from_profile(bytes_alg: int):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_hash") != kernel_hash():
+    if vals.get("kernel_source_hash") != kernel_hash(COUNTER_SOURCES[workload]):
         return None
+    return vals
+
+
+def traffic_from_profile(workload: str = "large_bf16"):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    vals = counter_values(workload)
     try:
-        return int(float(vals["hbm_bytes_per_launch"]))
+        return int(float(vals["hbm_bytes_per_launch"])) if vals else None
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_ratio(workload: str):
+    """Counter traffic over algorithmic bytes from the committed summary (None
+    if it is missing or was taken on other kernel code)."""
+    vals = counter_values(workload)
+    try:
+        return float(vals["traffic_over_algorithmic"]) if vals else None
     except (KeyError, ValueError):
         return None
 
@@ -87,9 +123,25 @@ def timed_calls(fn, n, stream):
     return start.elapsed_time(stop) / n  # ms per call
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(dp, seconds: float):
-    """The CPU oracle on a bounded sample of the same workload: consecutive
-    layers of the first listed request, every head, until `seconds` pass."""
+    """The CPU oracle on a bounded sample of the same workload: the tiles of
+    the first listed request, (layer, head) by (layer, head).  Timed twice:
+    on one thread (the plain loop), then with one task per tile on a thread
+    pool as wide as this process's CPU share (the C oracle releases the GIL),
+    each for about half of `seconds`.  Only the oracle calls are timed (host
+    copies of the tiles are made first)."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     import rssm_inputs as ri
     import torch
@@ -99,28 +151,60 @@ def cpu_baseline(dp, seconds: float):
     _, _, d_x, d_B, d_dt = ri.dense_sizes(spec)
     sb, ib = ri.ELEM_BYTES[spec.state_dtype], ri.ELEM_BYTES[spec.input_dtype]
     k, r0 = int(m.prefix[b]), int(m.ring_start[b])
-    done_bytes, spent, tiles, layers = 0, 0.0, 0, 0
+    tile_bytes = (2 * spec.H * n_tile * sb + k * (spec.H * spec.dim * ib + spec.G * spec.dstate * ib + spec.H * 4)) / spec.H
+    host = lambda t: (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy()  # noqa: E731
+    layers = {}
+
+    def layer(l):
+        if l not in layers:
+            s = int(m.src[l, b])
+            layers[l] = (host(dp.state[l][s, :spec.H * n_tile]).view(np.uint16), host(dp.x[l][s, :d_x]).view(np.uint16),
+                         host(dp.Bm[l][s, :d_B]).view(np.uint16), dp.dt[l][s, :d_dt].cpu().numpy(), dp.A[l].cpu().numpy())
+        return layers[l]
+
+    def run(unit):
+        l, h = unit
+        src, x, B, dt, A = layers[l]
+        oracle.tile(spec, l, b, h, r0, k, float(A[h]), src[h * n_tile:(h + 1) * n_tile], None, x, B, dt)
+
+    units = [(l, h) for l in range(spec.L) for h in range(spec.H)]
+    half = seconds / 2
+    # single thread: consecutive tiles until half the budget is spent
+    done1, spent1 = 0, 0.0
     for l in range(spec.L):
-        s = int(m.src[l, b])
-        host = lambda t: (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy()  # noqa: E731
-        src = host(dp.state[l][s, :spec.H * n_tile]).view(np.uint16)
-        x = host(dp.x[l][s, :d_x]).view(np.uint16)
-        B = host(dp.Bm[l][s, :d_B]).view(np.uint16)
-        dt = dp.dt[l][s, :d_dt].cpu().numpy()
-        A = dp.A[l].cpu().numpy()
+        layer(l)
         t0 = time.perf_counter()
         for h in range(spec.H):
-            oracle.tile(spec, l, b, h, r0, k, float(A[h]), src[h * n_tile:(h + 1) * n_tile], None, x, B, dt)
-        spent += time.perf_counter() - t0
-        tiles += spec.H
-        layers += 1
-        done_bytes += 2 * spec.H * n_tile * sb + k * (spec.H * spec.dim * ib + spec.G * spec.dstate * ib + spec.H * 4)
-        if spent >= seconds:
+            run((l, h))
+        spent1 += time.perf_counter() - t0
+        done1 += spec.H
+        if spent1 >= half:
             break
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"request {b} (k={k}), layers 0..{layers - 1}, all {spec.H} heads: {tiles} tiles of "
-                      f"{spec.dim}x{spec.dstate}, {done_bytes} algorithmic bytes in {spent:.1f} s, single thread",
-            "seconds": round(spent, 2)}
+    rate1 = done1 / spent1   # tiles per second on one thread
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:
+        share = os.cpu_count() or 1
+    threads = max(1, min(share, int(os.environ.get("OMP_NUM_THREADS", share)), 16))
+    # all threads: the next tiles, sized to about half the budget at the ideal speed-up
+    n_multi = min(len(units), max(threads * 4, int(rate1 * threads * half)))
+    todo = units[done1:done1 + n_multi] if done1 + n_multi <= len(units) else units[:n_multi]
+    for l in sorted(set(u[0] for u in todo)):
+        layer(l)
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(run, todo))
+        spent_n = time.perf_counter() - t0
+    rate_n = len(todo) / spent_n
+    gbs = lambda tiles_per_s: round(tiles_per_s * tile_bytes / 1e9, 4)  # noqa: E731
+    return {"value": gbs(rate_n), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"request {b} (k={k}), tiles of {spec.dim}x{spec.dstate} ({tile_bytes:.0f} algorithmic bytes "
+                      f"each): {done1} tiles on one thread in {spent1:.1f} s, then {len(todo)} tiles on "
+                      f"{threads} threads in {spent_n:.1f} s",
+            "threads": threads, "host_cores": os.cpu_count(), "cpu_share": share, "cpu_model": _cpu_model(),
+            "single_thread": {"value": gbs(rate1), "unit": "GB/s", "tiles": done1, "seconds": round(spent1, 2)},
+            "all_threads": {"value": gbs(rate_n), "unit": "GB/s", "tiles": len(todo), "seconds": round(spent_n, 2),
+                            "speedup_over_single": round(rate_n / rate1, 2)}}
 
 
 def main():
@@ -136,9 +220,11 @@ def main():
     ap.add_argument("--all-pad-only", action="store_true",
                     help="profile mode: 200 calls with every request listed and every source the pad slot")
     ap.add_argument("--pmc-calibrate", action="store_true",
-                    help="counter mode: 2 full-batch calls, then 2 plain device copies of 1 GiB")
-    ap.add_argument("--workload", default=WORKLOAD, choices=["large_bf16", "large_i8", "large_f8sr"],
-                    help="workload of the profile modes (the headline line always uses large_bf16)")
+                    help="counter mode: 2 calls of --workload, then 2 plain device copies of 1 GiB; prints "
+                         "the workload's algorithmic bytes per call as one JSON line")
+    ap.add_argument("--workload", default=WORKLOAD, choices=sorted(COUNTER_KERNEL),
+                    help="workload of the profile modes (the headline line always uses large_bf16); "
+                         "checkpoints, gdn_large and ssu_large in --pmc-calibrate only")
     ap.add_argument("--only-gdn", action="store_true",
                     help="profile mode: the gated-delta-rule commit line only")
     ap.add_argument("--plain-alloc", action="store_true",
@@ -151,8 +237,9 @@ def main():
                     help="skip the multi-checkpoint (flush + checkpoint) line")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the int8 and e4m3+Philox workload lines")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="print the HBM-traffic summary of two --pmc-calibrate counter runs and exit")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "ALG_JSON"),
+                    help="print the HBM-traffic summary of two --pmc-calibrate counter runs (and the JSON "
+                         "line one of them printed) and exit")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="print the kernel-stats table of a --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
@@ -181,6 +268,11 @@ def main():
         # the pools physically contiguous (before the process allocates anything)
         rp.use_contiguous_allocator()
     dev = torch.device("cuda:0")
+    if args.pmc_calibrate and args.workload in ("gdn_large", "ssu_large"):
+        pmc_calibrate_other(args.workload, dev)
+        return
+    if args.workload in ("gdn_large", "ssu_large", "checkpoints") and not args.pmc_calibrate:
+        raise SystemExit(f"--workload {args.workload} is a counter-mode workload (--pmc-calibrate)")
     if args.only_gdn:
         print(json.dumps({"gdn_commit": gdn_workload(dev, torch.cuda.current_stream(), args.steps, with_null=False)}), flush=True)
         return
@@ -190,6 +282,8 @@ def main():
     profile_mode = (args.only_main or args.empty_only or args.all_pad_only or args.pmc_calibrate
                     or args.only_checkpoints)
     wl = args.workload if profile_mode else WORKLOAD
+    if wl == "checkpoints":
+        wl = "large_bf16"   # the two-checkpoint call runs on the large_bf16 problem
     spec = ri.CONFIGS[wl]
     say("generating", wl, "seed", SEEDS[wl])
     t0 = time.time()
@@ -221,12 +315,17 @@ def main():
             for _ in range(200):
                 pad_call()
         else:
+            if args.workload == "checkpoints":
+                dst, pre = hx.flush_and_checkpoint_tables(dp.meta)
+                call = hx.prepared_checkpoints(dp, tabs, torch.from_numpy(dst).to(dev), torch.from_numpy(pre).to(dev))
+                nbytes = hx.checkpoint_bytes(spec, dp.meta, dst, pre)
+            else:
+                nbytes = full_bytes
             for _ in range(2):
                 call()
-            a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-            b_ = torch.empty_like(a)
-            for _ in range(2):
-                b_.copy_(a)
+            calibration_copies(dev)
+            print(json.dumps({"counter_workload": args.workload, "algorithmic_bytes": nbytes,
+                              "kernel": COUNTER_KERNEL[args.workload]}), flush=True)
         torch.cuda.synchronize()
         say("done")
         return
@@ -251,7 +350,7 @@ def main():
                    "algorithmic_bytes_per_call": full_bytes,
                    "pools": "hipMalloc" if args.plain_alloc else "physically contiguous (rssm_pool.h)"},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(full_bytes),
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("large_bf16"),
                      "kernel": "materialize_kernel<bf16,bf16,64x128,kmax8>", "kernel_source_hash": kernel_hash()},
         "us_per_request_full": round(ms * 1e3 / spec.B, 3),
         "single_call_ms_min_med_max": [round(singles[0], 3), round(singles[2], 3), round(singles[-1], 3)],
@@ -375,6 +474,45 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def calibration_copies(dev):
+    """Two plain device copies of 1 GiB (1 GiB read and 1 GiB written each):
+    the counter readings they produce scale counter KiB to bytes."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    b_ = torch.empty_like(a)
+    for _ in range(2):
+        b_.copy_(a)
+    torch.cuda.synchronize()
+
+
+def pmc_calibrate_other(workload, dev):
+    """Counter mode for the gated-delta-rule commit and the decode step: 2 calls
+    on the full-size problem, then the calibration copies."""
+    import torch
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    import replayssm_persistent_rssm_amd as rp
+    if workload == "gdn_large":
+        spec = ri.GDN_CONFIGS["gdn_large"]
+        dp = ri.make_gdn_device_problem(spec, 1010, dev)
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+        call = rp.GdnCommitCall(dp.state, dp.rawv, dp.rawk, dp.g, dp.beta, i32(dp.state_indices),
+                                i32(dp.accept_lens), track_state_indices=i32(dp.track_state_indices),
+                                track_steps=i32(dp.track_steps), null_block_id=spec.null_block_id)
+        nbytes = hx.gdn_bytes(spec, dp.state_indices, dp.accept_lens, dp.track_state_indices, dp.track_steps)
+    else:
+        spec = ri.SSU_CONFIGS["ssu_large"]
+        dp = ri.make_ssu_device_problem(spec, 1020, dev)
+        call = hx.ssu_prepared(dp)
+        nbytes = hx.ssu_bytes(spec, dp.slots_np, dp.num_buffered_np)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        call()
+    calibration_copies(dev)
+    print(json.dumps({"counter_workload": workload, "algorithmic_bytes": nbytes,
+                      "kernel": COUNTER_KERNEL[workload]}), flush=True)
+
+
 def checkpoint_workload(dp, tabs, spec, stream, steps):
     """The large_bf16 problem with two checkpoints per request: every buffered
     token flushed in place plus the state at half the prefix written to the
@@ -410,7 +548,8 @@ def checkpoint_workload(dp, tabs, spec, stream, steps):
            "GB/s": round(nbytes / (ms_multi * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms_multi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "two_single_calls_ms": round(ms_two, 4),
-           "speedup_vs_two_calls": round(ms_two / ms_multi, 3)}
+           "speedup_vs_two_calls": round(ms_two / ms_multi, 3),
+           "traffic_over_algorithmic": traffic_ratio("checkpoints")}
     say(f"checkpoints: {out}")
     return out
 
@@ -445,7 +584,8 @@ def gdn_workload(dev, stream, steps, with_null: bool = True):
            "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "us_per_request": round(ms * 1e3 / max(live, 1), 3)}
+           "us_per_request": round(ms * 1e3 / max(live, 1), 3),
+           "traffic_over_algorithmic": traffic_ratio("gdn_large")}
     # every request null: the work discovery alone (nothing is written); left
     # out in the profile mode, whose trace then holds only the full calls
     if not with_null:
@@ -496,7 +636,8 @@ def ssu_workload(dev, stream, steps):
            "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "us_per_request": round(ms * 1e3 / max(live, 1), 3)}
+           "us_per_request": round(ms * 1e3 / max(live, 1), 3),
+           "traffic_over_algorithmic": traffic_ratio("ssu_large")}
     say(f"ssu_decode: {out}")
     del call, dp
     torch.cuda.empty_cache()
@@ -526,7 +667,8 @@ def other_workload(name, dev, stream, steps):
            "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "us_per_request": round(ms * 1e3 / n, 3)}
+           "us_per_request": round(ms * 1e3 / n, 3),
+           "traffic_over_algorithmic": traffic_ratio(name)}
     say(f"{name}: {out}")
     del call, tabs, dp
     torch.cuda.empty_cache()
@@ -547,11 +689,35 @@ def _counter_rows(path, counter):
     return [rows[d] for d in sorted(rows)]
 
 
-def counters_summary(fetch_csv, write_csv):
-    """HBM traffic of the headline kernel from FETCH_SIZE and WRITE_SIZE runs of
+COUNTER_DESCRIPTION = {
+    "large_bf16": "materialize_kernel<bf16 state, bf16 input, 64x128, kmax 8> on the large_bf16 workload "
+                  "(48 layers, 256 active requests, 256 heads of 64x128 bf16)",
+    "large_i8": "materialize_kernel<int8 state, fp16 input, 64x128, kmax 8> on the large_i8 workload "
+                "(48 layers, 64 active requests, a quarter with k = 0, 256 heads of 64x128 int8 + fp32 row scales)",
+    "large_f8sr": "materialize_kernel<e4m3 state, bf16 input, 64x128, kmax 16, Philox-10 stochastic rounding> on "
+                  "the large_f8sr workload (48 layers, 128 active requests, 128 heads of 64x128 e4m3 + fp32 row scales)",
+    "checkpoints": "materialize_kernel<bf16, bf16, 64x128, kmax 8, 4 checkpoints> on large_bf16 with two "
+                   "checkpoints per request (in-place flush of all k tokens + the state after k//2 tokens)",
+    "gdn_large": "gdn_commit_kernel<8> on gdn_large (48 layers, 256 requests, 32 value heads over 16 key heads, "
+                 "fp32 128x128 states, 8-token bf16 windows, tracked steps)",
+    "ssu_large": "ssu_decode_kernel<bf16, bf16, 4> on ssu_large (one layer, 256 requests, 256 heads of 64x128 bf16 "
+                 "checkpoints, 4 new tokens)",
+}
+
+
+def counters_summary(fetch_csv, write_csv, alg_json):
+    """HBM traffic of one kernel from FETCH_SIZE and WRITE_SIZE runs of
     `--pmc-calibrate` (KiB per dispatch).  The run ends with two 1 GiB device
     copies (1 GiB read and 1 GiB written each): their readings give the factor
-    from counter KiB to bytes that is applied to the materialize dispatches."""
+    from counter KiB to bytes that is applied to the kernel's dispatches."""
+    info = None
+    for line in open(alg_json):
+        line = line.strip()
+        if line.startswith("{") and "counter_workload" in line:
+            info = json.loads(line)
+    if info is None:
+        raise SystemExit(f"{alg_json}: no counter_workload line")
+    wl, alg, kname = info["counter_workload"], int(info["algorithmic_bytes"]), info["kernel"]
     fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
     write = _counter_rows(write_csv, "WRITE_SIZE")
     gib_kib = float(1 << 20)
@@ -559,32 +725,28 @@ def counters_summary(fetch_csv, write_csv):
     facs = []
     for rows, what in ((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE")):
         copies = [v for n, v in rows if "copyBuffer" in n][-2:]
-        mats = [v for n, v in rows if "materialize_kernel" in n]
+        mats = [v for n, v in rows if kname in n]
         if len(copies) != 2 or not mats:
-            raise SystemExit(f"{what}: expected 2 calibration copies and materialize dispatches")
+            raise SystemExit(f"{what}: expected 2 calibration copies and {kname} dispatches")
         facs.append((what, copies, mats, gib_kib / (sum(copies) / 2)))
-    import rssm_inputs as ri
-    import rssm_harness as hx
-    spec = ri.CONFIGS[WORKLOAD]
-    alg = hx.algorithmic_bytes(spec, ri.make_meta(spec, np.random.default_rng(SEEDS[WORKLOAD])))
     rd = sum(facs[0][2]) / len(facs[0][2]) * facs[0][3] * 1024
     wr = sum(facs[1][2]) / len(facs[1][2]) * facs[1][3] * 1024
     repo = "$REPO"
-    out.append("# HBM traffic of materialize_kernel<bf16 state, bf16 input, 64x128, kmax 8> on the large_bf16 workload")
-    out.append("# (48 layers, 256 active requests, 256 heads of 64x128 bf16; one full-batch call per dispatch)")
+    out.append(f"# HBM traffic of {COUNTER_DESCRIPTION[wl]}; one call per dispatch")
     out.append("# commands (REPO = repository root on the GPU box):")
     for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         out.append(f"#   cd /tmp && rocprofv3 --pmc {c} --output-format csv -d /tmp/pmc_{d} -o {d} -- "
-                   f"python3 {repo}/bench.py --pmc-calibrate")
+                   f"python3 {repo}/bench.py --pmc-calibrate --workload {wl} > /tmp/alg_{d}.json")
     out.append(f"#   python3 {repo}/bench.py --summarize-counters /tmp/pmc_fetch/fetch_counter_collection.csv "
-               "/tmp/pmc_write/write_counter_collection.csv")
+               "/tmp/pmc_write/write_counter_collection.csv /tmp/alg_fetch.json")
     out.append("# calibration: the run ends with two torch copy_ of 1 GiB (__amd_rocclr_copyBuffer: 1 GiB read, "
                "1 GiB written)")
     for what, copies, mats, fac in facs:
         out.append(f"#   {what} per copy: {copies[0]:.1f}, {copies[1]:.1f} KiB -> factor {fac:.4f}")
-    out.append("# materialize dispatches: FETCH_SIZE " + ", ".join(f"{v:.1f}" for v in facs[0][2])
+    out.append(f"# {kname} dispatches: FETCH_SIZE " + ", ".join(f"{v:.1f}" for v in facs[0][2])
                + " KiB; WRITE_SIZE " + ", ".join(f"{v:.1f}" for v in facs[1][2]) + " KiB")
-    out.append(f"kernel_source_hash: {kernel_hash()}")
+    out.append(f"counter_workload: {wl}")
+    out.append(f"kernel_source_hash: {kernel_hash(COUNTER_SOURCES[wl])}")
     out.append(f"fetch_factor: {facs[0][3]:.4f}")
     out.append(f"write_factor: {facs[1][3]:.4f}")
     out.append(f"hbm_read_bytes_per_launch: {rd:.0f}")

@@ -17,9 +17,11 @@
  * Nothing here crosses the ABI but plain C types.  Every pointer inside
  * rssm_materialize_tables is DEVICE memory owned by the caller; the call
  * allocates nothing, keeps no reference after it returns, and reads no
- * device memory on the host (it never synchronises).  (rssm_pool.h offers
- * physically contiguous memory for the pools.)  The caller keeps
+ * device memory on the host (it never synchronises).  The caller keeps
  * every buffer alive until the enqueued work has completed on the stream.
+ * (rssm_pool.h, a placement helper outside this boundary, hands out
+ * physically contiguous device memory for the pools; the operation works on
+ * any device memory.)
  */
 #ifndef RSSM_MATERIALIZE_H
 #define RSSM_MATERIALIZE_H
@@ -63,7 +65,8 @@ typedef enum {
  *   state_dtype      RSSM_F32 | RSSM_BF16 | RSSM_F16 | RSSM_I8 | RSSM_F8E4M3
  *   input_dtype      x and B ring dtype: RSSM_F32 | RSSM_BF16 | RSSM_F16
  *   a_dtype          A dtype: RSSM_F32 (dt is always fp32)
- *   max_workgroups   0: the resident capacity (four times it for one-byte state;
+ *   max_workgroups   0: the default grid (the resident capacity; a multiple
+ *                    of it for one-byte state, see rssm_materialize_launch_config;
  *                    the work loop is persistent); > 0: exactly this many
  *                    workgroups (results do not depend on it) */
 typedef struct {
@@ -172,19 +175,37 @@ rssm_status rssm_materialize_checkpoints(const rssm_materialize_desc *desc,
                                          const rssm_materialize_tables *tables,
                                          int32_t num_checkpoints, void *hip_stream);
 
-/* Text of the last non-OK status returned on the calling thread ("" if none).
- * The pointer stays valid until the next call on that thread. */
+/* Text of the last non-OK status returned on the calling thread ("" if none):
+ * which host-validation rule failed, or the HIP runtime's error string.  The
+ * pull-request page ("Replayssm prefix materialize", change table) lists host
+ * validation and runtime error checks as part of the operation; a C ABI
+ * returns the status and keeps the text here instead of raising.  The
+ * pointer stays valid until the next call on that thread; no other state is
+ * kept. */
 const char *rssm_last_error(void);
 
 /* The launch the call would make for `desc` on the current device: grid and
- * block size in threads, and static LDS bytes per workgroup.  Validates desc
- * like rssm_materialize; queries the device (may return RSSM_ERR_HIP). */
+ * block size in threads, and static LDS bytes per workgroup.  This is the
+ * occupancy-based launch sizing of the pull-request page's change table
+ * ("Replayssm prefix materialize"): the grid is the device's compute units
+ * times the workgroups of this instance one compute unit holds (times 8 for
+ * one-byte state, whose requests differ more in cost), or
+ * desc->max_workgroups when that is > 0.  grid, block, lds_bytes: host
+ * int32 outputs, all non-NULL.  Validates desc like rssm_materialize
+ * (RSSM_ERR_INVALID_ARGUMENT / RSSM_ERR_UNSUPPORTED before any HIP call);
+ * queries the device (may return RSSM_ERR_HIP).  Enqueues nothing. */
 rssm_status rssm_materialize_launch_config(const rssm_materialize_desc *desc,
                                            int32_t *grid, int32_t *block, int32_t *lds_bytes);
 
 /* Test hook: run the kernel's own encode step on caller-given fp32 rows, so
  * that rounding (nearest-even and Philox stochastic) can be compared bit for
- * bit.  rows: device [n][dstate] fp32; coords: device [n][4] int32 = (layer,
+ * bit.  The rounding is the one the materialize page's Parameters select
+ * (rand_seed, philox_rounds: stochastic rounding with Philox when the round
+ * count is positive) with the key and counter derivation of the pull-request
+ * page's change table ("Philox seed derivation"), read as: key = the seed's
+ * two 32-bit halves, counter = ((row * dstate + column) / 4, head, physical
+ * request, layer), word column mod 4 per element.
+ * rows: device [n][dstate] fp32; coords: device [n][4] int32 = (layer,
  * physical request, head, row) used as Philox coordinates; rand_seed: device
  * int64[1] (NULL when philox_rounds == 0); out_codes: device [n][dstate] in
  * state_dtype; out_scales: device [n] fp32 for one-byte state, else NULL.

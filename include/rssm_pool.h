@@ -2,13 +2,20 @@
  * rssm_pool.h -- physically contiguous device memory for the state pools of
  * librssm_materialize (MI355X, gfx950).
  *
- * Not an operation of the pages: a placement helper for the pools that the
- * materialize, commit and decode kernels stream (tens of GiB per layer set).
+ * Not an operation of the pages and not part of the operation's boundary
+ * (rssm_materialize.h): a placement helper for the pools that the
+ * materialize, commit and decode kernels stream (tens of GiB per layer set),
+ * used by the benchmark and the tests to place their pools.  The operation
+ * entry points accept any device memory and allocate nothing themselves; only
+ * these helpers allocate.
  * Measured on MI355X, a plain hipMalloc of a large pool in the first process
  * on a box can land on physical memory that streams markedly slower than a
  * physically contiguous allocation: a 20 GiB device copy ran at 4.7 TB/s
- * against 5.7 TB/s, and the 48-layer bf16 materialize at 19.4 ms against
- * 17.2 ms.  These entry points allocate with hipDeviceMallocContiguous and
+ * against 5.7 TB/s, and the 48-layer bf16 materialize at 19.4 ms (67-68% of
+ * the 8 TB/s HBM peak) against 17.2 ms (76-77%): the 70% roofline fraction
+ * of that workload holds with contiguous pools, not with plain allocations
+ * in a box's first process.  These entry points allocate with
+ * hipDeviceMallocContiguous and
  * fall back to hipMalloc when the device has no contiguous range that large.
  *
  * Plain C types only.  The memory belongs to the caller until freed with

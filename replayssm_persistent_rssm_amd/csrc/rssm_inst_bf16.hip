@@ -1,21 +1,9 @@
 // rssm_inst_bf16.hip -- compiled instances of the materialize and encode
 // kernels for bf16 state (one translation unit per state dtype so they build
 // in parallel).
-#include "rssm_kernel.h"
+#include "rssm_instances.h"
 
 namespace rssm {
-
-#define RSSM_KENTRY(ST, IT, D, S, KM, SR)                                              \
-  {ST, IT, D, S, KM, SR, 1, reinterpret_cast<const void*>(&materialize_kernel<ST, IT, D, S, KM, (SR != 0)>), \
-   "materialize<" #ST "," #IT "," #D "x" #S ",kmax" #KM ",sr" #SR ">"},
-// Multi-checkpoint instances (up to kMaxCheckpoints per request).
-#define RSSM_MENTRY(ST, IT, D, S, KM, SR)                                              \
-  {ST, IT, D, S, KM, SR, kMaxCheckpoints,                                             \
-   reinterpret_cast<const void*>(&materialize_kernel<ST, IT, D, S, KM, (SR != 0), kMaxCheckpoints>), \
-   "materialize_checkpoints<" #ST "," #IT "," #D "x" #S ",kmax" #KM ",sr" #SR ">"},
-#define RSSM_EENTRY(ST, S, SR)                                                           \
-  {ST, S, SR, reinterpret_cast<const void*>(&encode_rows_kernel<ST, S, (SR != 0)>),     \
-   "encode_rows<" #ST ",dstate" #S ",sr" #SR ">"},
 
 static const KernelEntry kKernels[] = {
     RSSM_KENTRY(kBF16, kF32, 16, 16, 8, 0)

@@ -372,7 +372,48 @@ def test_row_scales_correctly_rounded(dev):
 # --------------------------------------------------------------------------
 # Full-size workloads, sampled (launch configuration of the benchmark)
 # --------------------------------------------------------------------------
+def _pool_snapshot(dp, slot_sets):
+    """Byte copies (on the device) of the given slots of every layer's state
+    and scale pools; slot_sets[l] is a sorted list of slots of layer l."""
+    import torch
+    snap = []
+    for l, sl in enumerate(slot_sets):
+        idx = torch.tensor(sl, dtype=torch.long, device=dp.state[l].device)
+        st = dp.state[l].view(torch.uint8)[idx].clone() if sl else None
+        sc = dp.scale[l].view(torch.uint8)[idx].clone() if (sl and dp.scale) else None
+        snap.append((idx, st, sc))
+    return snap
+
+
+def _assert_snapshot_equal(dp, snap, what):
+    import torch
+    for l, (idx, st, sc) in enumerate(snap):
+        if st is None:
+            continue
+        assert torch.equal(dp.state[l].view(torch.uint8)[idx], st), f"{what}: layer {l} state bytes changed"
+        if sc is not None:
+            assert torch.equal(dp.scale[l].view(torch.uint8)[idx], sc), f"{what}: layer {l} scale bytes changed"
+
+
+def _assert_fill(dp, slot_sets, fill, what):
+    """Every byte of the given slots (state and scale pools) is the fill byte."""
+    import torch
+    for l, sl in enumerate(slot_sets):
+        if not sl:
+            continue
+        idx = torch.tensor(sl, dtype=torch.long, device=dp.state[l].device)
+        assert bool((dp.state[l].view(torch.uint8)[idx] == fill).all().item()), f"{what}: layer {l} state written"
+        if dp.scale:
+            assert bool((dp.scale[l].view(torch.uint8)[idx] == fill).all().item()), f"{what}: layer {l} scale written"
+
+
 def _sampled_full_size(dev, name, n_active, seed, n_samples=24, all_pad_after=False):
+    """One call on the full-size problem in the benchmark's launch
+    configuration.  Byte for byte: every slot of every layer outside the
+    listed requests' destinations keeps its bytes (the drawn source range is
+    compared with a device copy taken before the call; every other slot must
+    still hold the fill byte).  Sampled: listed (request, layer, head) tiles
+    against the oracle, tile by tile."""
     import torch
     import oracle
     import parity
@@ -383,72 +424,85 @@ def _sampled_full_size(dev, name, n_active, seed, n_samples=24, all_pad_after=Fa
     tabs = hx.tables(dp, dev)
     torch.cuda.synchronize()
     m = dp.meta
-    srcs = sorted(set(int(v) for v in m.src.reshape(-1) if v != spec.pad_slot_id))
-    before = [int(t[srcs].view(torch.int32).to(torch.int64).sum().item()) for t in dp.state]
+    listed = [int(v) for v in m.active[:n_active]]
+    if n_active < spec.B:
+        assert int(m.active[n_active]) == -1
+    pad = spec.pad_slot_id
+    # slots the generator drew (the source range), per layer; the rest holds 0xA5
+    drawn = sorted(set(int(v) for v in m.src.reshape(-1) if v != pad))
+    drawn = list(range(drawn[0], drawn[-1] + 1)) if drawn else []
+    dst_of = [sorted(int(m.dst[l, b]) for b in listed if m.src[l, b] != pad and m.dst[l, b] != pad)
+              for l in range(spec.L)]
+    fill_slots = [sorted(set(range(m.slots)) - set(drawn) - set(dst_of[l])) for l in range(spec.L)]
+    src_snap = _pool_snapshot(dp, [drawn] * spec.L)
+    torch.cuda.synchronize()
     hx.materialize(dp, tabs)
     torch.cuda.synchronize()
-    after = [int(t[srcs].view(torch.int32).to(torch.int64).sum().item()) for t in dp.state]
-    assert before == after, "source slots changed"
+    _assert_snapshot_equal(dp, src_snap, "source slots")
+    _assert_fill(dp, fill_slots, 0xA5, "slot outside the listed destinations")
 
-    rng = np.random.default_rng(seed)
-    n_tile = spec.dim * spec.dstate
-    _, _, d_x, d_B, d_dt = ri.dense_sizes(spec)
-    picks = [(0, 0, 0), (n_active - 1, spec.L - 1, spec.H - 1)]
-    picks += [(int(rng.integers(n_active)), int(rng.integers(spec.L)), int(rng.integers(spec.H)))
-              for _ in range(n_samples)]
-    np_dt = ri.STORAGE_NP[spec.state_dtype]
-    for i, l, h in picks:
-        b = int(m.active[i])
-        s, d = int(m.src[l, b]), int(m.dst[l, b])
-        k, r0 = int(m.prefix[b]), int(m.ring_start[b])
-        def host(t, sl):
-            a = t[sl].cpu()
-            if a.dtype == torch.bfloat16:
-                a = a.view(torch.int16)
-            return a.numpy()
-        src_tile = host(dp.state[l], (s, slice(h * n_tile, (h + 1) * n_tile))).view(np_dt)
-        gpu_tile = host(dp.state[l], (d, slice(h * n_tile, (h + 1) * n_tile))).view(np_dt)
-        src_sc = gpu_sc = None
-        if dp.scale:
-            src_sc = host(dp.scale[l], (s, slice(h * spec.dim, (h + 1) * spec.dim)))
-            gpu_sc = host(dp.scale[l], (d, slice(h * spec.dim, (h + 1) * spec.dim)))
-        x_slot = host(dp.x[l], (s, slice(0, d_x))).view(ri.STORAGE_NP[spec.input_dtype])
-        B_slot = host(dp.Bm[l], (s, slice(0, d_B))).view(ri.STORAGE_NP[spec.input_dtype])
-        dt_slot = host(dp.dt[l], (s, slice(0, d_dt)))
-        A_h = float(dp.A[l][h].item())
-        codes, scale, exact, mag = oracle.tile(spec, l, b, h, r0, k, A_h, src_tile, src_sc, x_slot, B_slot, dt_slot)
-        what = f"{name} i={i} b={b} l={l} h={h} k={k}"
-        if k == 0:
-            assert np.array_equal(gpu_tile.view(np.uint8), src_tile.view(np.uint8)), what
-            if gpu_sc is not None:
-                assert np.array_equal(gpu_sc.view(np.uint32), src_sc.view(np.uint32)), what
-        else:
-            parity.compare_tile(spec.state_dtype, gpu_tile, codes, exact, mag, gpu_sc, scale, what)
-    # destination slots of requests that are not listed keep their fill bytes
-    listed = set(int(v) for v in m.active[:n_active])
-    free_dst = sorted(set(range(spec.B, 2 * spec.B)) - set(int(v) for v in m.dst.reshape(-1)))
-    if free_dst:
-        for l in (0, spec.L - 1):
-            t = dp.state[l][free_dst[:4]].view(torch.uint8)
-            assert bool((t == 0xA5).all().item()), "an unlisted destination slot was written"
+    if n_active:
+        rng = np.random.default_rng(seed)
+        n_tile = spec.dim * spec.dstate
+        _, _, d_x, d_B, d_dt = ri.dense_sizes(spec)
+        picks = [(0, 0, 0), (n_active - 1, spec.L - 1, spec.H - 1)]
+        picks += [(int(rng.integers(n_active)), int(rng.integers(spec.L)), int(rng.integers(spec.H)))
+                  for _ in range(n_samples)]
+        np_dt = ri.STORAGE_NP[spec.state_dtype]
+        for i, l, h in picks:
+            b = int(m.active[i])
+            s, d = int(m.src[l, b]), int(m.dst[l, b])
+            k, r0 = int(m.prefix[b]), int(m.ring_start[b])
+
+            def host(t, sl):
+                a = t[sl].cpu()
+                if a.dtype == torch.bfloat16:
+                    a = a.view(torch.int16)
+                return a.numpy()
+            src_tile = host(dp.state[l], (s, slice(h * n_tile, (h + 1) * n_tile))).view(np_dt)
+            gpu_tile = host(dp.state[l], (d, slice(h * n_tile, (h + 1) * n_tile))).view(np_dt)
+            src_sc = gpu_sc = None
+            if dp.scale:
+                src_sc = host(dp.scale[l], (s, slice(h * spec.dim, (h + 1) * spec.dim)))
+                gpu_sc = host(dp.scale[l], (d, slice(h * spec.dim, (h + 1) * spec.dim)))
+            x_slot = host(dp.x[l], (s, slice(0, d_x))).view(ri.STORAGE_NP[spec.input_dtype])
+            B_slot = host(dp.Bm[l], (s, slice(0, d_B))).view(ri.STORAGE_NP[spec.input_dtype])
+            dt_slot = host(dp.dt[l], (s, slice(0, d_dt)))
+            A_h = float(dp.A[l][h].item())
+            codes, scale, exact, mag = oracle.tile(spec, l, b, h, r0, k, A_h, src_tile, src_sc, x_slot, B_slot,
+                                                   dt_slot)
+            what = f"{name} i={i} b={b} l={l} h={h} k={k}"
+            if k == 0:
+                assert np.array_equal(gpu_tile.view(np.uint8), src_tile.view(np.uint8)), what
+                if gpu_sc is not None:
+                    assert np.array_equal(gpu_sc.view(np.uint32), src_sc.view(np.uint32)), what
+            else:
+                parity.compare_tile(spec.state_dtype, gpu_tile, codes, exact, mag, gpu_sc, scale, what)
     if all_pad_after:
         # the same listed requests with every source slot the pad slot: the
-        # launch (the benchmark's all-pad call) must leave every pool byte as is
+        # launch (the benchmark's all-pad call) must leave every pool byte as
+        # is -- the source range against its copy, the written destinations
+        # against a copy taken now, everything else still the fill byte
         say("full size", name, "all listed, every source the pad slot")
-        pad_src = torch.full((spec.L, spec.B), spec.pad_slot_id, dtype=torch.int32, device=dev)
-        sums = [int(t.view(torch.int32).to(torch.int64).sum().item()) for t in dp.state]
+        dst_snap = _pool_snapshot(dp, dst_of)
+        pad_src = torch.full((spec.L, spec.B), pad, dtype=torch.int32, device=dev)
         hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "src_slots": pad_src}))()
         torch.cuda.synchronize()
-        assert sums == [int(t.view(torch.int32).to(torch.int64).sum().item()) for t in dp.state], \
-            "an all-pad call wrote"
-    del dp, tabs
+        _assert_snapshot_equal(dp, src_snap, "all-pad call: source slots")
+        _assert_snapshot_equal(dp, dst_snap, "all-pad call: destination slots")
+        _assert_fill(dp, fill_slots, 0xA5, "all-pad call: other slots")
+        del dst_snap
+    del src_snap, dp, tabs
     torch.cuda.empty_cache()
-    return listed
+    return set(listed)
 
 
-@pytest.mark.parametrize("n_active", [256, 16])
+@pytest.mark.parametrize("n_active", [256, 16, 1, 0])
 def test_full_size_large_bf16_sampled(dev, n_active):
-    _sampled_full_size(dev, "large_bf16", n_active, 1000 + 2 * 10 + n_active % 7, all_pad_after=n_active == 256)
+    """The large bf16 workload at every active count of its sweep (256, 16,
+    1, 0); a single request gets more sampled tiles."""
+    _sampled_full_size(dev, "large_bf16", n_active, 1000 + 2 * 10 + n_active % 7,
+                       n_samples=64 if n_active == 1 else 24, all_pad_after=n_active == 256)
 
 
 def test_full_size_large_i8_sampled(dev):
