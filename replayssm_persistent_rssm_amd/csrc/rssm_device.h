@@ -77,6 +77,38 @@ __device__ __forceinline__ void gstore(T* p, T v) {
   *(RSSM_GLOBAL T*)(p) = v;
 }
 
+// Buffer accesses: a 128-bit resource (base, size in bytes) held in scalar
+// registers, a 32-bit per-lane offset and a wave-uniform offset.  Compared
+// with 64-bit per-lane addresses this saves the address arithmetic and two
+// vector registers per live address; accesses at or past the size are
+// dropped (loads return 0).  The resource word 3 is the gfx9 raw-buffer
+// format; aux bit 1 requests the non-temporal (streaming) policy.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
+}
+
+template <bool NT>
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0u, 0u, 0)), v),
+                                         r, voff, soff, NT ? 2 : 0);
+}
+
+__device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ void bstore_f32(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+
 // NT: non-temporal (streaming) access, for data read or written once.
 template <int DT, bool NT = false>
 __device__ __forceinline__ Chunk<DT> load_chunk(const char* p) {
@@ -172,12 +204,25 @@ __device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_
 }
 
 // Two Philox4x32-R blocks with counters (x, y, z, w) and (x + 1, y, z, w),
-// interleaved for instruction-level parallelism; rounds are unrolled by two.
+// interleaved for instruction-level parallelism; rounds are unrolled by two
+// (fully for the common count of 10).
 __device__ __forceinline__ void philox4x32_pair(uint32_t x, uint32_t y, uint32_t z, uint32_t w, uint32_t k0,
                                                 uint32_t k1, int rounds, uint32_t (&u)[8]) {
   constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
   uint32_t a0 = x, a1 = y, a2 = z, a3 = w;
   uint32_t b0 = x + 1u, b1 = y, b2 = z, b3 = w;
+  if (rounds == 10) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      philox_round(a0, a1, a2, a3, k0, k1);
+      philox_round(b0, b1, b2, b3, k0, k1);
+      k0 += kW0;
+      k1 += kW1;
+    }
+    u[0] = a0; u[1] = a1; u[2] = a2; u[3] = a3;
+    u[4] = b0; u[5] = b1; u[6] = b2; u[7] = b3;
+    return;
+  }
   int i = 0;
   for (; i + 2 <= rounds; i += 2) {
     philox_round(a0, a1, a2, a3, k0, k1);
@@ -214,14 +259,6 @@ __device__ __forceinline__ void sr_words(uint32_t (&u)[8], int r, int c0, int ds
 __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
   const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
-  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
-// Byte 3 of a, b, c, d as one little-endian word (bit 7 of each byte is the
-// sign bit of the corresponding fp32 value).
-__device__ __forceinline__ uint32_t pack_high_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0703u);
-  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0703u);
   return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
@@ -319,18 +356,20 @@ __device__ __forceinline__ uint32_t i8_round(float t, bool stochastic, uint32_t 
   return static_cast<uint32_t>(q) & 0xFFu;
 }
 
-// Magnitude code of stochastic e4m3 rounding for a = |t| with
-// 2^-6 <= a < 464 only (callers check the range for the whole wave first);
-// abits are the bits of a (sign clear).  In the normal range e4m3 keeps the
-// top 3 mantissa bits and the 20 dropped bits d are f * 2^20, so the rule
-// rounds up iff u < d * 2^12, i.e. iff (u >> 12) < d, i.e. iff adding
-// 0xFFFFF - (u >> 12) = (u >> 12) ^ 0xFFFFF to the bits carries into bit 20,
-// the lowest kept bit.  Bits 30..20 (exponent and kept mantissa) then hold
-// the rounded value; subtracting 960 << 20 rebiases the exponent (bias 127
-// to bias 7), and the result saturates at 448 (code 0x7E).
-__device__ __forceinline__ uint32_t e4m3_sr_normal_mag(uint32_t abits, uint32_t u) {
-  const uint32_t v = abits + ((u >> 12) ^ 0xFFFFFu) - (960u << 20);
-  return min(v >> 20, 0x7Eu);
+// Stochastic e4m3 rounding of a row-scaled value t with 2^-6 <= |t| (and t
+// not NaN; callers check the range for the whole wave first), returned as
+// the exactly representable fp32 value the code stands for.  |t| is first
+// clamped to 448 (the saturating rule; 448's dropped bits are zero, so it
+// never rounds up).  In the normal range e4m3 keeps the top 3 mantissa bits
+// and the 20 dropped bits d are f * 2^20; adding (u >> 12) ^ 0xFFFFF =
+// 0xFFFFF - (u >> 12) carries into bit 20 iff (u >> 12) < d, which is the
+// rule u < f * 2^32, and clearing the dropped bits then leaves the rounded
+// value (a carry out of the mantissa moves to the next binade).  The sign
+// bit is never reached: the clamped magnitude's bits are below 2^30.
+__device__ __forceinline__ float e4m3_sr_normal_value(float t, uint32_t u) {
+  const float c = __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
+  const uint32_t x = __float_as_uint(c) + ((u >> 12) ^ 0xFFFFFu);
+  return __uint_as_float(x & 0xFFF00000u);
 }
 
 // General e4m3 rounding (any input): nearest-even or stochastic, saturating;

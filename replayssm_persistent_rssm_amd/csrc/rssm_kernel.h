@@ -259,31 +259,30 @@ __device__ __forceinline__ Chunk<ST> encode_chunk(const float (&acc)[8], const u
         // NaN elements (ignored by the row max) and elements below 2^-6 (where
         // the subnormal grid applies) are rare: one compare finds both, and a
         // wavefront holding any takes the general rule for all its elements.
-        // The common path works on |t| = |acc| * inv and takes the sign bits
-        // from acc (inv > 0): bit 7 of byte 3 of each fp32 value is its sign,
-        // which goes to bit 7 of its code byte.
-        uint32_t code[8];
-        float ta[8];
+        // The common path rounds each value onto the e4m3 grid as an fp32
+        // value (e4m3_sr_normal_value) and converts it with the hardware
+        // conversion, which is exact for values on the grid and places the
+        // sign and the codes in their bytes.
         bool rare = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ta[i] = fabsf(acc[i]) * inv;
-          rare |= !(ta[i] >= 0x1p-6f);
-        }
+        for (int i = 0; i < 8; ++i) rare |= !(fabsf(t[i]) >= 0x1p-6f);
         if (__builtin_expect(__ballot(rare) != 0, 0)) {
+          uint32_t code[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) code[i] = e4m3_round(t[i], true, u[i]);
           out.w[0] = pack_low_bytes(code[0], code[1], code[2], code[3]);
           out.w[1] = pack_low_bytes(code[4], code[5], code[6], code[7]);
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) code[i] = e4m3_sr_normal_mag(__float_as_uint(ta[i]), u[i]);
-#pragma unroll
           for (int w = 0; w < 2; ++w) {
-            const uint32_t sg = pack_high_bytes(__float_as_uint(acc[4 * w]), __float_as_uint(acc[4 * w + 1]),
-                                                __float_as_uint(acc[4 * w + 2]), __float_as_uint(acc[4 * w + 3]));
-            out.w[w] = (sg & 0x80808080u) |
-                       pack_low_bytes(code[4 * w], code[4 * w + 1], code[4 * w + 2], code[4 * w + 3]);
+            // (the high half of the first conversion's old operand is
+            // overwritten by the second: any dead register serves)
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sr_normal_value(t[4 * w], u[4 * w]),
+                                                     e4m3_sr_normal_value(t[4 * w + 1], u[4 * w + 1]),
+                                                     static_cast<int>(u[4 * w]), false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sr_normal_value(t[4 * w + 2], u[4 * w + 2]),
+                                                 e4m3_sr_normal_value(t[4 * w + 3], u[4 * w + 3]), pk, true);
+            out.w[w] = static_cast<uint32_t>(pk);
           }
         }
       } else if (any_nan()) {
@@ -371,11 +370,18 @@ struct DefaultTune {
   static constexpr int kChunkItems = 16;       // 0: one contiguous item range per wavefront;
                                                // > 0: chunks of this many items dealt round-robin
   static constexpr int kWavesPerSimd = 0;      // register budget; 0: the rule above
+  static constexpr bool kMfmaOneByte = true;   // one-byte state: fold on the matrix cores
 };
+
+// One-byte state with one checkpoint folds on the matrix cores (see
+// mfma_fold_heads), unless a tuning variant turns it off.
+template <class Tune, int ST, int NCK>
+constexpr bool kMfmaFold = Tune::kMfmaOneByte && kOneByte<ST> && NCK == 1;
 
 template <class Tune, int KMAX, int ST, int IT, int NCK>
 constexpr int waves_per_simd() {
-  return Tune::kWavesPerSimd > 0 ? Tune::kWavesPerSimd : kWavesPerSimd<KMAX, ST, IT, NCK>;
+  return Tune::kWavesPerSimd > 0 ? Tune::kWavesPerSimd
+                                 : (kMfmaFold<Tune, ST, NCK> ? 4 : kWavesPerSimd<KMAX, ST, IT, NCK>);
 }
 
 // Checkpoint bookkeeping of one (request, layer): kc[c] is the prefix length of
@@ -393,6 +399,394 @@ __device__ __forceinline__ void sort_checkpoints(int (&kc)[NCK], int (&dc)[NCK])
       dc[j] = sw ? dc[j + 1] : d0;
       kc[j + 1] = sw ? k0 : kc[j + 1];
       dc[j + 1] = sw ? d0 : dc[j + 1];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One-byte state: the fold on the matrix cores.
+//
+// With one-byte state and stochastic rounding the path is bound by VALU
+// issue, not by HBM: per state element Philox-10 costs about 10
+// instructions and the fold k fused multiply-adds, against about 9.8
+// instructions' worth of issue time per element at HBM speed.  The fold is
+// a rank-k update of the tile, U = W X^T B with k <= 16, i.e. a small dense
+// contraction: these instances run it as fp32 16x16x4 MFMAs, which execute
+// on the matrix cores beside the VALU work (Philox, row scales, encode).
+//
+// Layout.  A tile is 4 blocks of 16 rows.  In a row block, lane L holds row
+// j = L % 16 and, with q = L / 16, the 32 columns [16q, 16q + 16) and
+// [64 + 16q, 64 + 16q + 16): two 16-byte loads per lane, each instruction
+// covering 64 contiguous bytes of 16 rows.  Those 32 columns are the
+// accumulator of 8 MFMAs (blocks bb = 0..7, 4 registers each): register v of
+// block bb holds column col(q, bb, v) = 64 (bb / 4) + 16 q + 4 (bb % 4) + v,
+// so block bb's 4 registers are 4 consecutive columns (one output dword,
+// one Philox block) and blocks 0..3 / 4..7 fill the two 16-byte chunks in
+// memory order.  For the 16x16x4 fp32 MFMA, D[i][j] sits in lane
+// j + 16 (i / 4), register i % 4, and lane L supplies A[L % 16][L / 16] and
+// B[L / 16][L % 16]; with D[i][j] = U[row j][col(i / 4, bb, i % 4)] the
+// operands are A[i][t] = B_t[col(i / 4, bb, i % 4)] (ring B rows: fixed per
+// head group and lane, held in registers) and B[t][j] = w_t x_t[row j]
+// (staged per head in LDS as [token][row]).  C is the decoded source times
+// its decay, so one MFMA chain per block gives D S + U.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The [token][row] LDS staging of w_t x_t: 64 floats per token, row r of
+// token t stored at position r ^ (16 (t & 1)), so that the two token rows a
+// half-wavefront reads (tokens 4 ks, 4 ks + 1; rows 16 rb .. 16 rb + 15)
+// fall into disjoint banks.
+constexpr int kWxStride = 64;
+__device__ __forceinline__ int wx_pos(int t, int row) { return t * kWxStride + (row ^ (16 * (t & 1))); }
+
+// LDS floats per wavefront of the matrix-core fold: the w_t x_t staging, and
+// the A operands of k-steps 1 .. KMAX/4 - 1 as [k-step - 1][lane][block]
+// (k-step 0 stays in registers).
+template <int KMAX>
+constexpr int kMfmaLds = KMAX * kWxStride + (KMAX / 4 - 1) * 64 * 8;
+
+// One element of the ring's B rows as fp32.
+template <int IT>
+__device__ __forceinline__ float load_elem(const char* p) {
+  if constexpr (IT == kF32) {
+    return gload(reinterpret_cast<const float*>(p));
+  } else if constexpr (IT == kBF16) {
+    return __uint_as_float(static_cast<uint32_t>(gload(reinterpret_cast<const uint16_t*>(p))) << 16);
+  } else {
+    return f16_bits_to_float(gload(reinterpret_cast<const uint16_t*>(p)));
+  }
+}
+
+// Four one-byte codes (one dword, byte v = column v) decoded and multiplied
+// by d: the source value times its decay.  int8: the bytes biased by 128 are
+// converted as unsigned, and fma(u, d, -128 d) rounds (u - 128) d once, the
+// same bits as code * d.
+template <int ST>
+__device__ __forceinline__ f32x4 decode4_scaled(uint32_t w, float d) {
+  f32x4 r;
+  if constexpr (ST == kI8) {
+    const uint32_t u = w ^ 0x80808080u;
+    const float nd = -128.0f * d;
+    r[0] = fmaf(static_cast<float>(u & 0xFFu), d, nd);
+    r[1] = fmaf(static_cast<float>((u >> 8) & 0xFFu), d, nd);
+    r[2] = fmaf(static_cast<float>((u >> 16) & 0xFFu), d, nd);
+    r[3] = fmaf(static_cast<float>(u >> 24), d, nd);
+  } else {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    r[0] = lo[0] * d;
+    r[1] = lo[1] * d;
+    r[2] = hi[0] * d;
+    r[3] = hi[1] * d;
+  }
+  return r;
+}
+
+// Encode one row block held in the MFMA layout: acc[bb][v] is column
+// col(q, bb, v) of row r.  The row max runs over the lane's 32 values and
+// then over the 4 lanes holding row r (lanes r % 16 + 16 q'); out[bb] is the
+// dword of block bb's 4 codes, rs the new row scale.  Every lane of the
+// wavefront must execute this.
+template <int ST, bool SR>
+__device__ __forceinline__ void encode_rowblock(f32x4 (&acc)[8], int r, int q, int h, int b, int l,
+                                                uint32_t key0, uint32_t key1, int rounds, uint32_t (&out)[8],
+                                                float& rs) {
+  constexpr int qmax = (ST == kI8) ? 127 : 448;
+  float m = 0.0f;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) m = fmaxf(m, fabsf(acc[bb][v]));
+  // values >= +0 and never NaN: their bits order as unsigned integers.  The
+  // lanes of row r are L, L ^ 16, L ^ 32, L ^ 48: gfx950's row swaps give
+  // each lane its partner's value one and two rows of 16 away.
+  uint32_t mu = __float_as_uint(m);
+  {
+    const auto p16 = __builtin_amdgcn_permlane16_swap(mu, mu, false, false);
+    mu = max(p16[0], p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(mu, mu, false, false);
+    mu = max(p32[0], p32[1]);
+  }
+  m = __uint_as_float(mu);
+  float inv;
+  const bool ok = row_quant<qmax>(m, rs, inv);
+  // Elements that take the general rule: NaN (all encodes), and for
+  // stochastic e4m3 any |t| below 2^-6 (the subnormal grid).  The smallest
+  // |t| is the smallest |S'| times inv (rounding is monotonic), and NaN is
+  // found two elements per unordered compare.
+  bool has_nan = false;
+  float mn = fabsf(acc[0][0]);
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    has_nan |= __builtin_isunordered(acc[bb][0], acc[bb][1]) || __builtin_isunordered(acc[bb][2], acc[bb][3]);
+    if constexpr (SR && ST == kF8)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mn = fminf(mn, fabsf(acc[bb][v]));
+  }
+  bool rare = false;
+  if constexpr (SR && ST == kF8) rare = !(mn * inv >= 0x1p-6f);
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[bb][v] *= inv;   // t = S' * (qmax / rowmax)
+  const bool general = __builtin_expect(__ballot(has_nan || rare) != 0, 0);
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb) {
+    // blocks 2pb and 2pb + 1: Philox counters x and x + 1 (counter word 0 is
+    // (r * dstate + c) / 4 for the block's first column c)
+    uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if constexpr (SR) {
+      const uint32_t x = static_cast<uint32_t>(32 * r + 16 * (pb >> 1) + 4 * q + 2 * (pb & 1));
+      philox4x32_pair(x, static_cast<uint32_t>(h), static_cast<uint32_t>(b), static_cast<uint32_t>(l), key0, key1,
+                      rounds, u);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int bb = 2 * pb + s;
+      const f32x4 t = acc[bb];
+      uint32_t w;
+      if constexpr (ST == kI8) {
+        if (SR || general) {
+          w = pack_low_bytes(i8_round(t[0], SR, u[4 * s]), i8_round(t[1], SR, u[4 * s + 1]),
+                             i8_round(t[2], SR, u[4 * s + 2]), i8_round(t[3], SR, u[4 * s + 3]));
+        } else {
+          // |t| <= 127 (1 + 2^-24)^2 < 127.5 in a valid row: one rounding to an
+          // integer, the low byte of the sum's bits is the code
+          w = pack_low_bytes(__float_as_uint(t[0] + 12582912.0f), __float_as_uint(t[1] + 12582912.0f),
+                             __float_as_uint(t[2] + 12582912.0f), __float_as_uint(t[3] + 12582912.0f));
+        }
+      } else if constexpr (SR) {
+        if (general) {
+          w = pack_low_bytes(e4m3_round(t[0], true, u[4 * s]), e4m3_round(t[1], true, u[4 * s + 1]),
+                             e4m3_round(t[2], true, u[4 * s + 2]), e4m3_round(t[3], true, u[4 * s + 3]));
+        } else {
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sr_normal_value(t[0], u[4 * s]),
+                                                   e4m3_sr_normal_value(t[1], u[4 * s + 1]),
+                                                   static_cast<int>(u[4 * s]), false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sr_normal_value(t[2], u[4 * s + 2]),
+                                               e4m3_sr_normal_value(t[3], u[4 * s + 3]), pk, true);
+          w = static_cast<uint32_t>(pk);
+        }
+      } else {
+        if (general) {
+          w = pack_low_bytes(e4m3_round(t[0], false, 0u), e4m3_round(t[1], false, 0u), e4m3_round(t[2], false, 0u),
+                             e4m3_round(t[3], false, 0u));
+        } else {
+          // hardware nearest-even conversion, equal to e4m3_round for |t| < 464
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], pk, true);
+          w = static_cast<uint32_t>(pk);
+        }
+      }
+      out[bb] = ok ? w : 0u;
+    }
+  }
+}
+
+// The heads [h0, h1) of one (request, layer) with k > 0 on the matrix-core
+// fold (one-byte state, 64 x 128 tiles, one checkpoint).  wxT: this
+// wavefront's LDS, kMfmaLds<KMAX> floats.
+template <int ST, int IT, int KMAX, bool SR, bool NTL, bool NTS>
+__device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, float* wxT, int h0, int h1, int k,
+                                                int r0, int b, int l, const char* src_state, char* dst_state,
+                                                const float* src_scale, float* dst_scale, const char* x_slot,
+                                                const char* B_slot, const float* dt_slot, const float* A,
+                                                uint32_t key0, uint32_t key1) {
+  constexpr int DIM = 64, DSTATE = 128;
+  constexpr int IB = Fmt<IT>::bytes;
+  constexpr int64_t kTile = static_cast<int64_t>(DIM) * DSTATE;   // bytes (one-byte state)
+  constexpr int NKS = KMAX / 4;                                     // k-steps of 4 tokens
+  constexpr int RBB = 16 * DSTATE;                                  // bytes per row block
+  constexpr int XCH = DIM / 8;
+  constexpr int XREP = (KMAX * XCH + 63) / 64;
+  const int G = a.H / a.hpg;
+  const int j = lane & 15, q = lane >> 4;
+  const uint32_t loff = static_cast<uint32_t>(j * DSTATE + 16 * q);
+  const int e_lane = (r0 + lane) % a.R;
+  const int nks = (k + 3) >> 2;
+  const int k4 = nks * 4;
+
+  float* amL = wxT + KMAX * kWxStride;   // A operands of k-steps >= 1
+  for (int g = h0 / a.hpg; g * a.hpg < h1; ++g) {
+    // A operands: lane L supplies B_t[col] for token t = 4 ks + L / 16 and
+    // column col(i / 4, bb, i % 4), i = L % 16; zero for tokens at or past k.
+    // k-step 0 in registers, the others in this wavefront's LDS.
+    float Am[8];
+    {
+      float av[NKS][8];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int t = 4 * ks + q;
+        const int e = ring_entry(r0, t < k ? t : 0, a.R);
+        const char* row = B_slot + (static_cast<int64_t>(e) * G + g) * DSTATE * IB;
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+          const int col = 64 * (bb >> 2) + 16 * (j >> 2) + 4 * (bb & 3) + (j & 3);
+          const float v = load_elem<IT>(row + col * IB);
+          av[ks][bb] = t < k ? v : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) Am[bb] = av[0][bb];
+      if constexpr (NKS > 1) {
+        wave_lds_fence();   // the previous group's reads of amL are done
+#pragma unroll
+        for (int ks = 1; ks < NKS; ++ks) {
+          f32x4* dst = reinterpret_cast<f32x4*>(amL + ((ks - 1) * 64 + lane) * 8);
+          dst[0] = f32x4{av[ks][0], av[ks][1], av[ks][2], av[ks][3]};
+          dst[1] = f32x4{av[ks][4], av[ks][5], av[ks][6], av[ks][7]};
+        }
+      }
+    }
+    const int hb = max(h0, g * a.hpg);
+    const int he = min(h1, (g + 1) * a.hpg);
+    // Each head's x rows, dt and A are requested one head ahead (right after
+    // the previous head has staged its own), and its first two row blocks
+    // during the previous head's last two: a head starts with its inputs
+    // arrived or in flight.
+    Chunk<IT> xraw[XREP];
+    float A_n = 0.0f, dt_n = 0.0f;
+    auto issue_small = [&](int hn) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rep = 0; rep < XREP; ++rep) {
+        const int idx = lane + 64 * rep;
+        const int tj = min(idx / XCH, 63);
+        const int ej = __shfl(e_lane, tj < k ? tj : 0);
+        xraw[rep] = load_chunk<IT>(x_slot + ((static_cast<int64_t>(ej) * a.H + hn) * DIM + (idx % XCH) * 8) * IB);
+      }
+      A_n = gload(A + hn);
+      if (lane < k) dt_n = gload(dt_slot + static_cast<int64_t>(e_lane) * a.H + hn);
+    };
+    const uint32_t soff = static_cast<uint32_t>(j) * 4;   // this lane's row scale in a row block
+    u32x4 s0[2], s1[2];
+    float ssc[2];
+    {
+      const rsrc_t rs_src = make_rsrc(src_state + hb * kTile, static_cast<uint32_t>(kTile));
+      const rsrc_t rs_ssc = make_rsrc(src_scale + static_cast<int64_t>(hb) * DIM, DIM * 4);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        s0[p] = bload16<NTL>(rs_src, loff, p * RBB);
+        s1[p] = bload16<NTL>(rs_src, loff, p * RBB + 64);
+        ssc[p] = bload_f32(rs_ssc, soff, p * 64);
+      }
+    }
+    issue_small(hb);
+    for (int h = hb; h < he; ++h) {
+      const bool more = h + 1 < he;
+      // the head's tiles and row scales (and the next head's) as buffer
+      // resources in scalar registers
+      const rsrc_t rs_src = make_rsrc(src_state + h * kTile, static_cast<uint32_t>(kTile));
+      const rsrc_t rs_dst = make_rsrc(dst_state + h * kTile, static_cast<uint32_t>(kTile));
+      const rsrc_t rs_ssc = make_rsrc(src_scale + static_cast<int64_t>(h) * DIM, DIM * 4);
+      const rsrc_t rs_dsc = make_rsrc(dst_scale + static_cast<int64_t>(h) * DIM, DIM * 4);
+      const rsrc_t rs_nsrc = make_rsrc(src_state + (h + 1) * kTile, more ? static_cast<uint32_t>(kTile) : 0u);
+      const rsrc_t rs_nssc = make_rsrc(src_scale + static_cast<int64_t>(h + 1) * DIM, more ? DIM * 4 : 0u);
+      const float A_h = A_n;
+      float dtj = 0.0f, aj = 1.0f;
+      if (lane < k) {
+        dtj = dt_n;
+        aj = expf(dtj * A_h);
+      }
+      // suffix products over the tokens: D = prod a_j, w_j = dt_j prod_{u>j} a_u
+      float P = aj;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float o = __shfl_down(P, off);
+        if (lane + off < 16) P *= o;
+      }
+      float Pn = __shfl_down(P, 1);
+      if (lane + 1 >= 16) Pn = 1.0f;
+      const float w = dtj * Pn;
+      const float D = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P), 0));
+      // stage w_t x_t[row] as [token][row]; tokens k .. k4-1 get -0 weights
+      // (with A = +0 their products are -0, which leave every accumulator,
+      // including the sign of a zero, unchanged)
+      wave_lds_fence();
+#pragma unroll
+      for (int rep = 0; rep < XREP; ++rep) {
+        const int idx = lane + 64 * rep;
+        const int tj = min(idx / XCH, 63);
+        const float wj = __shfl(w, tj);
+        if (idx < k4 * XCH) {
+          const int r8 = (idx % XCH) * 8;
+          float xv[8];
+          decode_chunk<IT>(xraw[rep], xv);
+          f32x4 lo, hi;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            lo[u] = tj < k ? wj * xv[u] : -0.0f;
+            hi[u] = tj < k ? wj * xv[4 + u] : -0.0f;
+          }
+          *reinterpret_cast<f32x4*>(wxT + wx_pos(tj, r8)) = lo;       // 8 rows stay contiguous
+          *reinterpret_cast<f32x4*>(wxT + wx_pos(tj, r8) + 4) = hi;
+        }
+      }
+      wave_lds_fence();
+      if (more) issue_small(h + 1);   // xraw is free again
+
+      // row blocks in pairs (slot 0 and slot 1 of the two in flight); the
+      // pair loop stays rolled, which keeps register pressure down
+#pragma unroll 1
+      for (int rp = 0; rp < DIM / 16; rp += 2)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const int rb = rp + sl;
+        const float d0 = ssc[sl] * D;
+        f32x4 acc[8];
+        acc[0] = decode4_scaled<ST>(s0[sl].x, d0);
+        acc[1] = decode4_scaled<ST>(s0[sl].y, d0);
+        acc[2] = decode4_scaled<ST>(s0[sl].z, d0);
+        acc[3] = decode4_scaled<ST>(s0[sl].w, d0);
+        acc[4] = decode4_scaled<ST>(s1[sl].x, d0);
+        acc[5] = decode4_scaled<ST>(s1[sl].y, d0);
+        acc[6] = decode4_scaled<ST>(s1[sl].z, d0);
+        acc[7] = decode4_scaled<ST>(s1[sl].w, d0);
+        // the slot's bytes are decoded: its registers take the block two ahead
+        // (kept after the decode, so that no copy of the slot is needed)
+        __builtin_amdgcn_sched_barrier(0);
+        if (rb + 2 < DIM / 16) {
+          s0[sl] = bload16<NTL>(rs_src, loff, (rb + 2) * RBB);
+          s1[sl] = bload16<NTL>(rs_src, loff, (rb + 2) * RBB + 64);
+          ssc[sl] = bload_f32(rs_ssc, soff, (rb + 2) * 64);
+        } else if (more) {
+          // the next head's row blocks 0 and 1
+          s0[sl] = bload16<NTL>(rs_nsrc, loff, (rb + 2 - DIM / 16) * RBB);
+          s1[sl] = bload16<NTL>(rs_nsrc, loff, (rb + 2 - DIM / 16) * RBB + 64);
+          ssc[sl] = bload_f32(rs_nssc, soff, (rb + 2 - DIM / 16) * 64);
+        }
+        int kk = nks;
+        asm volatile("" : "+s"(kk));
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          if (ks < kk) {
+            const float bm = wxT[wx_pos(4 * ks + q, 16 * rb + j)];
+            float am[8];
+            if (ks == 0) {
+#pragma unroll
+              for (int bb = 0; bb < 8; ++bb) am[bb] = Am[bb];
+            } else {
+              const f32x4* src = reinterpret_cast<const f32x4*>(amL + ((ks > 0 ? ks - 1 : 0) * 64 + lane) * 8);
+              const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                am[u] = lo[u];
+                am[4 + u] = hi[u];
+              }
+            }
+#pragma unroll
+            for (int bb = 0; bb < 8; ++bb) acc[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[bb], bm, acc[bb], 0, 0, 0);
+          }
+        }
+        uint32_t out[8];
+        float rs = 0.0f;
+        encode_rowblock<ST, SR>(acc, 16 * rb + j, q, h, b, l, key0, key1, a.rounds, out, rs);
+        bstore16<NTS>(rs_dst, loff, rb * RBB, u32x4{out[0], out[1], out[2], out[3]});
+        bstore16<NTS>(rs_dst, loff, rb * RBB + 64, u32x4{out[4], out[5], out[6], out[7]});
+        if (q == 0) bstore_f32(rs_dsc, soff, rb * 64, rs);
+        // one row block at a time: interleaving the next block's decode and
+        // MFMAs into this block's encode would hold two sets of accumulators
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -427,10 +821,12 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
   static_assert(KMAX % 4 == 0 && KMAX <= 16, "KMAX");
   static_assert(NCK >= 1 && NCK <= 4, "NCK");
 
-  __shared__ __attribute__((aligned(16))) float lds_wx[kWaves][DIM * KMAX];
+  constexpr bool MF = kMfmaFold<Tune, ST, NCK>;
+  static_assert(!MF || (DIM == 64 && DSTATE == 128), "matrix-core fold: 64 x 128 tiles");
+  __shared__ __attribute__((aligned(16))) float lds_wx[kWaves][MF ? kMfmaLds<KMAX> : DIM * KMAX];
   constexpr int KREG = kBRegs<KMAX>;   // B rows of tokens below KREG in registers
   constexpr int KLDS = KMAX - KREG;     // the others in this wavefront's LDS, [token - KREG][column]
-  __shared__ __attribute__((aligned(16))) float lds_B[kWaves][KLDS > 0 ? KLDS * DSTATE : 4];
+  __shared__ __attribute__((aligned(16))) float lds_B[kWaves][(!MF && KLDS > 0) ? KLDS * DSTATE : 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
@@ -582,37 +978,63 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
     }
 
     if (k == 0) {
-      // Zero prefix: exact byte copy of each tile (and its row scales) to
-      // every live destination.
-      for (int h = h0; h < h1; ++h) {
-        const char* src_tile = src_state + h * kTile * SB;
+      // Zero prefix: exact byte copy of the heads' tiles (and row scales) to
+      // every live destination.  The tiles of heads h0 .. h1-1 of one slot
+      // are one contiguous range, copied as 1 KiB blocks, 16 bytes per lane
+      // (one-byte tiles streamed 8 bytes per lane, in their fold layout,
+      // copied at 5.3 TB/s on MI355X against 6.2 TB/s for 16 bytes per lane),
+      // four blocks in flight; the row scales are one float per lane.
+      constexpr int64_t kTileBytes = kTile * SB;
+      if constexpr (kTileBytes % 1024 == 0) {
+        constexpr int CPD = 4;
+        const int64_t nblk = (h1 - h0) * (kTileBytes / 1024);
+        const uint32_t boff = static_cast<uint32_t>(lane) * 16;
+        const char* sblk = src_state + h0 * kTileBytes;
 #pragma unroll 1
-        for (int p0 = 0; p0 < NPASS; p0 += PD) {
-          Chunk<ST> c[PD];
+        for (int64_t i0 = 0; i0 < nblk; i0 += CPD) {
+          u32x4 c[CPD];
 #pragma unroll
-          for (int q = 0; q < PD; ++q) {
-            const int r = rr + (p0 + q) * RPP;
-            if (kFull || r < DIM) c[q] = load_chunk<ST, NTL>(at(src_tile + (p0 + q) * PS, lane_off));
+          for (int q = 0; q < CPD; ++q)
+            if (i0 + q < nblk) c[q] = ld<NTL, u32x4>(at(sblk + (i0 + q) * 1024, boff));
+#pragma unroll
+          for (int q = 0; q < CPD; ++q) {
+            if (i0 + q < nblk) {
+#pragma unroll
+              for (int ck = 0; ck < NCK; ++ck)
+                if (kc[ck] == 0) st<NTS>(at(dst_state[ck] + h0 * kTileBytes + (i0 + q) * 1024, boff), c[q]);
+            }
           }
+        }
+      } else {
+        for (int h = h0; h < h1; ++h) {
+          const char* src_tile = src_state + h * kTileBytes;
+#pragma unroll 1
+          for (int p0 = 0; p0 < NPASS; p0 += PD) {
+            Chunk<ST> c[PD];
 #pragma unroll
-          for (int q = 0; q < PD; ++q) {
-            const int r = rr + (p0 + q) * RPP;
-            if (kFull || r < DIM) {
-              float sc = 0.0f;
-              if constexpr (Q) {
-                if (cc == 0) sc = gload(src_scale + h * DIM + r);
-              }
+            for (int q = 0; q < PD; ++q) {
+              const int r = rr + (p0 + q) * RPP;
+              if (kFull || r < DIM) c[q] = load_chunk<ST, NTL>(at(src_tile + (p0 + q) * PS, lane_off));
+            }
 #pragma unroll
-              for (int ck = 0; ck < NCK; ++ck) {
-                if (kc[ck] == 0) {
-                  store_chunk<ST, NTS>(at(dst_state[ck] + h * kTile * SB + (p0 + q) * PS, lane_off), c[q]);
-                  if constexpr (Q) {
-                    if (cc == 0) gstore(dst_scale[ck] + h * DIM + r, sc);
-                  }
-                }
+            for (int q = 0; q < PD; ++q) {
+              const int r = rr + (p0 + q) * RPP;
+              if (kFull || r < DIM) {
+#pragma unroll
+                for (int ck = 0; ck < NCK; ++ck)
+                  if (kc[ck] == 0) store_chunk<ST, NTS>(at(dst_state[ck] + h * kTileBytes + (p0 + q) * PS, lane_off), c[q]);
               }
             }
           }
+        }
+      }
+      if constexpr (Q) {
+        const int nsc = (h1 - h0) * DIM;
+        for (int i = lane; i < nsc; i += 64) {
+          const float sc = gload(src_scale + h0 * DIM + i);
+#pragma unroll
+          for (int ck = 0; ck < NCK; ++ck)
+            if (kc[ck] == 0) gstore(dst_scale[ck] + h0 * DIM + i, sc);
         }
       }
       continue;
@@ -625,6 +1047,11 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
     const float* dt_slot = reinterpret_cast<const float*>(uniform64(dt_raw)) +
                            static_cast<int64_t>(s) * uniform64(dts_raw);
     const float* A = reinterpret_cast<const float*>(uniform64(A_raw));
+    if constexpr (MF) {
+      mfma_fold_heads<ST, IT, KMAX, SR, NTL, NTS>(a, lane, wx, h0, h1, k, r0, b, l, src_state, dst_state[0],
+                                                  src_scale, dst_scale[0], x_slot, B_slot, dt_slot, A, key0, key1);
+      continue;
+    }
     const int e_lane = (r0 + lane) % a.R;  // ring entry of token `lane`
     // End of the segment that holds token `lane` (the shortest checkpoint
     // prefix above it); lanes at or past k hold no token.
