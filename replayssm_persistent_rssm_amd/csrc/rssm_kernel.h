@@ -167,6 +167,30 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
+// Value of lane (lane + N) within the lane's row of 16 (DPP row_shl:N), for
+// the token scans: tokens sit in lanes 0..15, and a lane only uses the value
+// when lane + N is a token lane of the same row.  No LDS round trip.
+template <int N>
+__device__ __forceinline__ float row_shl(float v) {
+  static_assert(N >= 1 && N <= 15, "row_shl");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x100 + N, 0xF, 0xF, true));
+}
+
+// Inclusive suffix products over the token lanes j < seg_end (<= 16): lane j
+// gets prod_{j <= u < seg_end} a_u; lanes at or past seg_end keep their value.
+__device__ __forceinline__ float suffix_products(float a, int lane, int seg_end) {
+  float P = a;
+  float o = row_shl<1>(P);
+  if (lane + 1 < seg_end) P *= o;
+  o = row_shl<2>(P);
+  if (lane + 2 < seg_end) P *= o;
+  o = row_shl<4>(P);
+  if (lane + 4 < seg_end) P *= o;
+  o = row_shl<8>(P);
+  if (lane + 8 < seg_end) P *= o;
+  return P;
+}
+
 // Max over the 16 lanes of an aligned lane group (one state row) of values
 // that are >= +0 and not NaN: swap lane pairs, then pairs of pairs
 // (quad_perm), then mirror within 8 lanes and within 16 lanes.  The bit
@@ -371,6 +395,7 @@ struct DefaultTune {
                                                // > 0: chunks of this many items dealt round-robin
   static constexpr int kWavesPerSimd = 0;      // register budget; 0: the rule above
   static constexpr bool kMfmaOneByte = true;   // one-byte state: fold on the matrix cores
+  static constexpr bool kMfmaPrefetch = false; // matrix-core fold: request the next head's inputs early
 };
 
 // One-byte state with one checkpoint folds on the matrix cores (see
@@ -586,7 +611,7 @@ __device__ __forceinline__ void encode_rowblock(f32x4 (&acc)[8], int r, int q, i
 // The heads [h0, h1) of one (request, layer) with k > 0 on the matrix-core
 // fold (one-byte state, 64 x 128 tiles, one checkpoint).  wxT: this
 // wavefront's LDS, kMfmaLds<KMAX> floats.
-template <int ST, int IT, int KMAX, bool SR, bool NTL, bool NTS>
+template <int ST, int IT, int KMAX, bool SR, bool NTL, bool NTS, bool PF>
 __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, float* wxT, int h0, int h1, int k,
                                                 int r0, int b, int l, const char* src_state, char* dst_state,
                                                 const float* src_scale, float* dst_scale, const char* x_slot,
@@ -651,7 +676,7 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
       for (int rep = 0; rep < XREP; ++rep) {
         const int idx = lane + 64 * rep;
         const int tj = min(idx / XCH, 63);
-        const int ej = __shfl(e_lane, tj < k ? tj : 0);
+        const int ej = ring_entry(r0, tj < k ? tj : 0, a.R);
         xraw[rep] = load_chunk<IT>(x_slot + ((static_cast<int64_t>(ej) * a.H + hn) * DIM + (idx % XCH) * 8) * IB);
       }
       A_n = gload(A + hn);
@@ -672,7 +697,18 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
     }
     issue_small(hb);
     for (int h = hb; h < he; ++h) {
-      const bool more = h + 1 < he;
+      const bool more = PF && h + 1 < he;
+      if (!PF && h > hb) {
+        const rsrc_t rs_src = make_rsrc(src_state + h * kTile, static_cast<uint32_t>(kTile));
+        const rsrc_t rs_ssc = make_rsrc(src_scale + static_cast<int64_t>(h) * DIM, DIM * 4);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          s0[p] = bload16<NTL>(rs_src, loff, p * RBB);
+          s1[p] = bload16<NTL>(rs_src, loff, p * RBB + 64);
+          ssc[p] = bload_f32(rs_ssc, soff, p * 64);
+        }
+        issue_small(h);
+      }
       // the head's tiles and row scales (and the next head's) as buffer
       // resources in scalar registers
       const rsrc_t rs_src = make_rsrc(src_state + h * kTile, static_cast<uint32_t>(kTile));
@@ -688,13 +724,8 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
         aj = expf(dtj * A_h);
       }
       // suffix products over the tokens: D = prod a_j, w_j = dt_j prod_{u>j} a_u
-      float P = aj;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const float o = __shfl_down(P, off);
-        if (lane + off < 16) P *= o;
-      }
-      float Pn = __shfl_down(P, 1);
+      const float P = suffix_products(aj, lane, 16);
+      float Pn = row_shl<1>(P);
       if (lane + 1 >= 16) Pn = 1.0f;
       const float w = dtj * Pn;
       const float D = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P), 0));
@@ -1048,7 +1079,7 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
                            static_cast<int64_t>(s) * uniform64(dts_raw);
     const float* A = reinterpret_cast<const float*>(uniform64(A_raw));
     if constexpr (MF) {
-      mfma_fold_heads<ST, IT, KMAX, SR, NTL, NTS>(a, lane, wx, h0, h1, k, r0, b, l, src_state, dst_state[0],
+      mfma_fold_heads<ST, IT, KMAX, SR, NTL, NTS, Tune::kMfmaPrefetch>(a, lane, wx, h0, h1, k, r0, b, l, src_state, dst_state[0],
                                                   src_scale, dst_scale[0], x_slot, B_slot, dt_slot, A, key0, key1);
       continue;
     }
@@ -1146,7 +1177,7 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
         for (int rep = 0; rep < XREP; ++rep) {
           const int idx = lane + 64 * rep;
           const int j = min(idx / XCH, 63);
-          const int ej = __shfl(e_lane, j < k ? j : 0);
+          const int ej = ring_entry(r0, j < k ? j : 0, a.R);
           xraw[rep] = load_chunk<IT>(x_slot + ((static_cast<int64_t>(ej) * a.H + h) * DIM + (idx % XCH) * 8) * IB);
         }
         const float A_h = gload(A + h);
@@ -1155,13 +1186,8 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
           dtj = gload(dt_slot + static_cast<int64_t>(e_lane) * a.H + h);
           aj = expf(dtj * A_h);
         }
-        float P = aj;  // inclusive suffix product over lanes j .. seg_end-1
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float o = __shfl_down(P, off);
-          if (lane + off < seg_end) P *= o;
-        }
-        float Pn = __shfl_down(P, 1);
+        const float P = suffix_products(aj, lane, seg_end);  // over lanes j .. seg_end-1
+        float Pn = row_shl<1>(P);
         if (lane + 1 >= seg_end) Pn = 1.0f;
         const float w = dtj * Pn;
         // Decay of the segment that ends at kc[c] (1 when no token is new).
