@@ -391,14 +391,17 @@ def main():
 
         sweep = {}
         t_empty = None
-        for n, reps in ((0, 1000), (1, 64), (16, 32), (256, max(4, args.steps // 2))):
+        for n, reps in ((0, 1000), (1, 256), (16, 64), (256, max(4, args.steps // 2))):
             # rotate the active set so the 256 MB last-level cache cannot serve it
             n_sets = 1 if n in (0, 256) else min(32, spec.B // n)
             sets = [active_list(perm[(j * n) % spec.B:(j * n) % spec.B + n]) for j in range(n_sets)]
+            # one prepared call per set: the timed loop makes one C call per step
+            calls_n = [hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "active_request_indices": a_}))
+                       for a_ in sets]
             it = [0]
 
             def rot():
-                call(sets[it[0] % n_sets])
+                calls_n[it[0] % n_sets]()
                 it[0] += 1
             for _ in range(3):
                 rot()
@@ -644,11 +647,51 @@ def ssu_workload(dev, stream, steps):
     return out
 
 
+def empty_launch_costs(dp, tabs, spec, stream):
+    """Cost of a call with nothing to do, in the workload's own launch
+    configuration: no active request (back-to-back calls on the stream, and
+    per call under graph replay), and every request listed with every source
+    slot the pad slot (back-to-back)."""
+    import torch
+    import rssm_harness as hx
+    dev = dp.state[0].device
+    empty = torch.full((spec.B,), -1, dtype=torch.int32, device=dev)
+    ecall = hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "active_request_indices": empty}))
+    for _ in range(20):
+        ecall()
+    torch.cuda.synchronize()
+    t_stream = timed_calls(ecall, 1000, stream)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        hx.prepared(dp, tabs)(empty)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        gcall = hx.prepared(dp, tabs)
+        for _ in range(100):
+            gcall(empty)
+    g.replay()
+    torch.cuda.synchronize()
+    t_graph = timed_calls(g.replay, 10, stream) / 100
+    pad_src = torch.full((spec.L, spec.B), spec.pad_slot_id, dtype=torch.int32, device=dev)
+    pcall = hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "src_slots": pad_src}))
+    for _ in range(20):
+        pcall()
+    torch.cuda.synchronize()
+    t_pad = timed_calls(pcall, 1000, stream)
+    del g
+    return {"empty_launch_us": round(t_stream * 1e3, 3), "empty_launch_us_graph": round(t_graph * 1e3, 3),
+            "empty_launch_us_all_pad": round(t_pad * 1e3, 3)}
+
+
 def other_workload(name, dev, stream, steps):
     """Time one call of a secondary workload (its listed requests active)."""
     import torch
     import rssm_harness as hx
     import rssm_inputs as ri
+    import replayssm_persistent_rssm_amd as rp
     spec = ri.CONFIGS[name]
     say("generating", name, "seed", SEEDS[name])
     dp = ri.make_device_problem(spec, SEEDS[name], dev, fill_dst=0)
@@ -669,6 +712,11 @@ def other_workload(name, dev, stream, steps):
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "us_per_request": round(ms * 1e3 / n, 3),
            "traffic_over_algorithmic": traffic_ratio(name)}
+    out.update(empty_launch_costs(dp, tabs, spec, stream))
+    out["grid"] = rp.rssm_materialize_launch_config(
+        num_layers=spec.L, batch=spec.B, num_heads=spec.H, heads_per_group=spec.hpg, dim=spec.dim,
+        dstate=spec.dstate, max_window=spec.W, ring_buffer_len=spec.R, state_dtype=spec.state_dtype,
+        input_dtype=spec.input_dtype)[0]
     say(f"{name}: {out}")
     del call, tabs, dp
     torch.cuda.empty_cache()

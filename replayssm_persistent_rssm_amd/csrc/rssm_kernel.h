@@ -396,6 +396,7 @@ struct DefaultTune {
   static constexpr int kWavesPerSimd = 0;      // register budget; 0: the rule above
   static constexpr bool kMfmaOneByte = true;   // one-byte state: fold on the matrix cores
   static constexpr bool kMfmaPrefetch = false; // matrix-core fold: request the next head's inputs early
+  static constexpr bool kMfmaTranspose = true; // matrix-core fold: coalesced row blocks through LDS
 };
 
 // One-byte state with one checkpoint folds on the matrix cores (see
@@ -467,8 +468,16 @@ __device__ __forceinline__ int wx_pos(int t, int row) { return t * kWxStride + (
 // LDS floats per wavefront of the matrix-core fold: the w_t x_t staging, and
 // the A operands of k-steps 1 .. KMAX/4 - 1 as [k-step - 1][lane][block]
 // (k-step 0 stays in registers).
-template <int KMAX>
-constexpr int kMfmaLds = KMAX * kWxStride + (KMAX / 4 - 1) * 64 * 8;
+template <int KMAX, bool TR>
+constexpr int kMfmaLds = KMAX * kWxStride + (KMAX / 4 - 1) * 64 * 8 + (TR ? 512 : 0);
+
+// Byte offset of 16-byte chunk c of row r in the 2 KiB LDS transposition
+// buffer of one 16-row block: chunk positions rotated by row (c ^ (r & 7)),
+// so that both the row-major writes (8 lanes per row) and the reads in the
+// accumulator layout (one row per lane, 8 rows at once) hit distinct banks.
+__device__ __forceinline__ uint32_t tr_pos(int r, int c) {
+  return static_cast<uint32_t>(r * 128 + 16 * (c ^ (r & 7)));
+}
 
 // One element of the ring's B rows as fp32.
 template <int IT>
@@ -610,8 +619,8 @@ __device__ __forceinline__ void encode_rowblock(f32x4 (&acc)[8], int r, int q, i
 
 // The heads [h0, h1) of one (request, layer) with k > 0 on the matrix-core
 // fold (one-byte state, 64 x 128 tiles, one checkpoint).  wxT: this
-// wavefront's LDS, kMfmaLds<KMAX> floats.
-template <int ST, int IT, int KMAX, bool SR, bool NTL, bool NTS, bool PF>
+// wavefront's LDS, kMfmaLds<KMAX, TR> floats.
+template <int ST, int IT, int KMAX, bool SR, bool NTL, bool NTS, bool PF, bool TR>
 __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, float* wxT, int h0, int h1, int k,
                                                 int r0, int b, int l, const char* src_state, char* dst_state,
                                                 const float* src_scale, float* dst_scale, const char* x_slot,
@@ -632,6 +641,14 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
   const int k4 = nks * 4;
 
   float* amL = wxT + KMAX * kWxStride;   // A operands of k-steps >= 1
+  // TR: the row blocks are loaded and stored as two coalesced 1 KiB halves
+  // (lane L: row L / 8 of the half, bytes 16 (L % 8) ..), and pass through a
+  // 2 KiB LDS buffer between that layout and the accumulator layout.  On
+  // MI355X a copy in the accumulator layout (16 rows x 64 bytes per
+  // instruction) streamed at 4.7 TB/s against 6.1 TB/s coalesced.
+  char* tT = reinterpret_cast<char*>(amL + (KMAX / 4 - 1) * 64 * 8);
+  const uint32_t voff = TR ? static_cast<uint32_t>(lane) * 16 : loff;   // per-lane offset of a row-block access
+  constexpr int HALF2 = TR ? 1024 : 64;                                  // offset of the second access
   for (int g = h0 / a.hpg; g * a.hpg < h1; ++g) {
     // A operands: lane L supplies B_t[col] for token t = 4 ks + L / 16 and
     // column col(i / 4, bb, i % 4), i = L % 16; zero for tokens at or past k.
@@ -690,8 +707,8 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
       const rsrc_t rs_ssc = make_rsrc(src_scale + static_cast<int64_t>(hb) * DIM, DIM * 4);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        s0[p] = bload16<NTL>(rs_src, loff, p * RBB);
-        s1[p] = bload16<NTL>(rs_src, loff, p * RBB + 64);
+        s0[p] = bload16<NTL>(rs_src, voff, p * RBB);
+        s1[p] = bload16<NTL>(rs_src, voff, p * RBB + HALF2);
         ssc[p] = bload_f32(rs_ssc, soff, p * 64);
       }
     }
@@ -703,8 +720,8 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
         const rsrc_t rs_ssc = make_rsrc(src_scale + static_cast<int64_t>(h) * DIM, DIM * 4);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          s0[p] = bload16<NTL>(rs_src, loff, p * RBB);
-          s1[p] = bload16<NTL>(rs_src, loff, p * RBB + 64);
+          s0[p] = bload16<NTL>(rs_src, voff, p * RBB);
+          s1[p] = bload16<NTL>(rs_src, voff, p * RBB + HALF2);
           ssc[p] = bload_f32(rs_ssc, soff, p * 64);
         }
         issue_small(h);
@@ -763,26 +780,34 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
       for (int sl = 0; sl < 2; ++sl) {
         const int rb = rp + sl;
         const float d0 = ssc[sl] * D;
+        u32x4 m0 = s0[sl], m1 = s1[sl];
+        if constexpr (TR) {
+          // row-major halves in, the lane's two chunks of row j out
+          *reinterpret_cast<u32x4*>(tT + tr_pos(lane >> 3, lane & 7)) = m0;
+          *reinterpret_cast<u32x4*>(tT + tr_pos(8 + (lane >> 3), lane & 7)) = m1;
+          m0 = *reinterpret_cast<const u32x4*>(tT + tr_pos(j, q));
+          m1 = *reinterpret_cast<const u32x4*>(tT + tr_pos(j, q + 4));
+        }
         f32x4 acc[8];
-        acc[0] = decode4_scaled<ST>(s0[sl].x, d0);
-        acc[1] = decode4_scaled<ST>(s0[sl].y, d0);
-        acc[2] = decode4_scaled<ST>(s0[sl].z, d0);
-        acc[3] = decode4_scaled<ST>(s0[sl].w, d0);
-        acc[4] = decode4_scaled<ST>(s1[sl].x, d0);
-        acc[5] = decode4_scaled<ST>(s1[sl].y, d0);
-        acc[6] = decode4_scaled<ST>(s1[sl].z, d0);
-        acc[7] = decode4_scaled<ST>(s1[sl].w, d0);
+        acc[0] = decode4_scaled<ST>(m0.x, d0);
+        acc[1] = decode4_scaled<ST>(m0.y, d0);
+        acc[2] = decode4_scaled<ST>(m0.z, d0);
+        acc[3] = decode4_scaled<ST>(m0.w, d0);
+        acc[4] = decode4_scaled<ST>(m1.x, d0);
+        acc[5] = decode4_scaled<ST>(m1.y, d0);
+        acc[6] = decode4_scaled<ST>(m1.z, d0);
+        acc[7] = decode4_scaled<ST>(m1.w, d0);
         // the slot's bytes are decoded: its registers take the block two ahead
         // (kept after the decode, so that no copy of the slot is needed)
         __builtin_amdgcn_sched_barrier(0);
         if (rb + 2 < DIM / 16) {
-          s0[sl] = bload16<NTL>(rs_src, loff, (rb + 2) * RBB);
-          s1[sl] = bload16<NTL>(rs_src, loff, (rb + 2) * RBB + 64);
+          s0[sl] = bload16<NTL>(rs_src, voff, (rb + 2) * RBB);
+          s1[sl] = bload16<NTL>(rs_src, voff, (rb + 2) * RBB + HALF2);
           ssc[sl] = bload_f32(rs_ssc, soff, (rb + 2) * 64);
         } else if (more) {
           // the next head's row blocks 0 and 1
-          s0[sl] = bload16<NTL>(rs_nsrc, loff, (rb + 2 - DIM / 16) * RBB);
-          s1[sl] = bload16<NTL>(rs_nsrc, loff, (rb + 2 - DIM / 16) * RBB + 64);
+          s0[sl] = bload16<NTL>(rs_nsrc, voff, (rb + 2 - DIM / 16) * RBB);
+          s1[sl] = bload16<NTL>(rs_nsrc, voff, (rb + 2 - DIM / 16) * RBB + HALF2);
           ssc[sl] = bload_f32(rs_nssc, soff, (rb + 2 - DIM / 16) * 64);
         }
         int kk = nks;
@@ -811,8 +836,16 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
         uint32_t out[8];
         float rs = 0.0f;
         encode_rowblock<ST, SR>(acc, 16 * rb + j, q, h, b, l, key0, key1, a.rounds, out, rs);
-        bstore16<NTS>(rs_dst, loff, rb * RBB, u32x4{out[0], out[1], out[2], out[3]});
-        bstore16<NTS>(rs_dst, loff, rb * RBB + 64, u32x4{out[4], out[5], out[6], out[7]});
+        u32x4 o0{out[0], out[1], out[2], out[3]}, o1{out[4], out[5], out[6], out[7]};
+        if constexpr (TR) {
+          // the lane's two chunks of row j in, row-major halves out
+          *reinterpret_cast<u32x4*>(tT + tr_pos(j, q)) = o0;
+          *reinterpret_cast<u32x4*>(tT + tr_pos(j, q + 4)) = o1;
+          o0 = *reinterpret_cast<const u32x4*>(tT + tr_pos(lane >> 3, lane & 7));
+          o1 = *reinterpret_cast<const u32x4*>(tT + tr_pos(8 + (lane >> 3), lane & 7));
+        }
+        bstore16<NTS>(rs_dst, voff, rb * RBB, o0);
+        bstore16<NTS>(rs_dst, voff, rb * RBB + HALF2, o1);
         if (q == 0) bstore_f32(rs_dsc, soff, rb * 64, rs);
         // one row block at a time: interleaving the next block's decode and
         // MFMAs into this block's encode would hold two sets of accumulators
@@ -854,7 +887,8 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
 
   constexpr bool MF = kMfmaFold<Tune, ST, NCK>;
   static_assert(!MF || (DIM == 64 && DSTATE == 128), "matrix-core fold: 64 x 128 tiles");
-  __shared__ __attribute__((aligned(16))) float lds_wx[kWaves][MF ? kMfmaLds<KMAX> : DIM * KMAX];
+  constexpr bool TR = Tune::kMfmaTranspose && KMAX <= 8;   // (16-token instances: LDS budget)
+  __shared__ __attribute__((aligned(16))) float lds_wx[kWaves][MF ? kMfmaLds<KMAX, TR> : DIM * KMAX];
   constexpr int KREG = kBRegs<KMAX>;   // B rows of tokens below KREG in registers
   constexpr int KLDS = KMAX - KREG;     // the others in this wavefront's LDS, [token - KREG][column]
   __shared__ __attribute__((aligned(16))) float lds_B[kWaves][(!MF && KLDS > 0) ? KLDS * DSTATE : 4];
@@ -1079,7 +1113,7 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
                            static_cast<int64_t>(s) * uniform64(dts_raw);
     const float* A = reinterpret_cast<const float*>(uniform64(A_raw));
     if constexpr (MF) {
-      mfma_fold_heads<ST, IT, KMAX, SR, NTL, NTS, Tune::kMfmaPrefetch>(a, lane, wx, h0, h1, k, r0, b, l, src_state, dst_state[0],
+      mfma_fold_heads<ST, IT, KMAX, SR, NTL, NTS, Tune::kMfmaPrefetch, TR>(a, lane, wx, h0, h1, k, r0, b, l, src_state, dst_state[0],
                                                   src_scale, dst_scale[0], x_slot, B_slot, dt_slot, A, key0, key1);
       continue;
     }
