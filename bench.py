@@ -716,7 +716,7 @@ def other_workload(name, dev, stream, steps):
     out["grid"] = rp.rssm_materialize_launch_config(
         num_layers=spec.L, batch=spec.B, num_heads=spec.H, heads_per_group=spec.hpg, dim=spec.dim,
         dstate=spec.dstate, max_window=spec.W, ring_buffer_len=spec.R, state_dtype=spec.state_dtype,
-        input_dtype=spec.input_dtype)[0]
+        input_dtype=spec.input_dtype, philox_rounds=spec.philox_rounds)[0]
     say(f"{name}: {out}")
     del call, tabs, dp
     torch.cuda.empty_cache()

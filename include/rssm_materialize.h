@@ -189,8 +189,8 @@ const char *rssm_last_error(void);
  * occupancy-based launch sizing of the pull-request page's change table
  * ("Replayssm prefix materialize"): the grid is the device's compute units
  * times the workgroups of this instance one compute unit holds (times 8 for
- * one-byte state, whose requests differ more in cost), or
- * desc->max_workgroups when that is > 0.  grid, block, lds_bytes: host
+ * one-byte state with stochastic rounding, whose requests differ more in
+ * cost), or desc->max_workgroups when that is > 0.  grid, block, lds_bytes: host
  * int32 outputs, all non-NULL.  Validates desc like rssm_materialize
  * (RSSM_ERR_INVALID_ARGUMENT / RSSM_ERR_UNSUPPORTED before any HIP call);
  * queries the device (may return RSSM_ERR_HIP).  Enqueues nothing. */

@@ -365,18 +365,20 @@ template <int KMAX> constexpr int kBRegs = (KMAX > 8) ? 4 : KMAX;
 template <int ST, int IT, int KMAX, int NCK>
 constexpr bool kMixB = (ST == kI8 && IT == kF16 && KMAX <= 8 && NCK == 1);
 
-// Resident wavefronts per SIMD the register budget is sized for.
+// Resident wavefronts per SIMD the register budget of the VALU fold is sized
+// for (two- and four-byte state, and every multi-checkpoint instance; the
+// one-byte single-checkpoint instances fold on the matrix cores at 4 waves).
 // e4m3 state adds software decode/encode on top of the row scales: its
 // 8-token instances get a 3-wave budget (168 registers) so they do not spill.
-// int8 keeps 4 waves (5 with packed fp16 B rows, above): it runs ~11% faster
-// than with 3 waves on MI355X, although the compiler then spills a few
-// registers outside the fold.
+// int8 keeps 4 waves (5 with packed fp16 B rows, above).
+// The multi-checkpoint instances (segment bookkeeping) get 3 waves, where
+// they do not spill (with windows up to 8, 4 waves spilled 32 registers and
+// the two-checkpoint large bf16 call ran 1% slower on MI355X).
 // 16-token instances get 4 waves, except with fp32 x/B (16 raw 32-byte B
-// chunks are held while a group's rows load) and the multi-checkpoint
-// instances (segment bookkeeping): 3 waves, where they do not spill.
+// chunks are held while a group's rows load): 3.
 template <int KMAX, int ST, int IT, int NCK>
 constexpr int kWavesPerSimd = (KMAX > 8) ? ((IT == kF32 || NCK > 1) ? 3 : 4)
-                                         : ((ST == kF8) ? 3 : (kMixB<ST, IT, KMAX, NCK> ? 5 : 4));
+                                         : ((ST == kF8 || NCK > 1) ? 3 : (kMixB<ST, IT, KMAX, NCK> ? 5 : 4));
 
 // Knobs of the state stream.  The library's instances use the defaults; the
 // alternatives exist so that streaming patterns can be compared on hardware.

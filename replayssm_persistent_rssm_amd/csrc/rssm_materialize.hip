@@ -245,16 +245,17 @@ rssm_status grid_for(const void* fn, int* grid_out) {
 // way).  A larger grid lets the hardware hand out workgroups as others
 // finish, which balances requests of different cost; every workgroup also
 // adds about 0.4 us per thousand to a call with nothing to do.  One-byte
-// state (its requests differ more in cost): eight times the resident
-// capacity, which on MI355X ran 2% (int8) and 6% (e4m3 + Philox) faster than
-// four times and 10-15% faster than one, for an empty call of about 5 us
-// under graph replay.  Other state: the resident capacity; eight times it was
-// 0.8% faster on bf16 but raised the empty call from 1.7 to 4.4 us.
+// state with stochastic rounding (bound by VALU issue, per-request cost
+// varying with the prefix length): eight times the resident capacity, which
+// on MI355X ran the e4m3 + Philox-10 workload in 5.00 ms against 5.24 ms at
+// four times and 5.86 ms at one (empty call 5.9 us against about 3.3 us).
+// Other state, including one-byte state with nearest-even rounding: the
+// resident capacity (int8 workload 2.30 ms at one, 2.29 ms at eight times).
 rssm_status materialize_grid(const rssm_materialize_desc* d, const void* fn, int* grid_out) {
   int resident = 0;
   rssm_status st = grid_for(fn, &resident);
   if (st != RSSM_OK) return st;
-  *grid_out = one_byte(d->state_dtype) ? 8 * resident : resident;
+  *grid_out = (one_byte(d->state_dtype) && d->philox_rounds > 0) ? 8 * resident : resident;
   return RSSM_OK;
 }
 

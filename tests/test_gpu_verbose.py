@@ -57,3 +57,30 @@ def test_verbose_prints_one_line_per_launch():
 @pytest.mark.parametrize("value", [None, "0"])
 def test_quiet_without_verbose(value):
     assert _run(value) == []
+
+
+def _launch_config(**kw):
+    import replayssm_persistent_rssm_amd as rp
+    base = dict(num_layers=2, batch=4, num_heads=8, heads_per_group=1, dim=64, dstate=128, max_window=16,
+                ring_buffer_len=16, input_dtype="bf16")
+    base.update(kw)
+    return rp.rssm_materialize_launch_config(**base)
+
+
+@pytest.mark.parametrize("state_dtype", ["i8", "f8e4m3"])
+def test_launch_config_grid_rule(state_dtype):
+    """Default grid: the instance's resident capacity (a whole multiple of the
+    compute units), eight times it for one-byte state with stochastic
+    rounding (a separate instance, whose resident capacity is again a
+    multiple of the compute units); max_workgroups replaces either."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g0, b0, s0 = _launch_config(state_dtype=state_dtype, philox_rounds=0)
+    g1, b1, s1 = _launch_config(state_dtype=state_dtype, philox_rounds=10)
+    print(f"[gpu-launch] {state_dtype}: rne grid {g0}, sr grid {g1}, cus {cus}", flush=True)
+    assert g0 > 0 and g0 % cus == 0
+    assert b1 == b0 == 256 and g1 % 8 == 0 and (g1 // 8) % cus == 0
+    assert _launch_config(state_dtype=state_dtype, philox_rounds=10, max_workgroups=37)[0] == 37
+    assert _launch_config(state_dtype=state_dtype, philox_rounds=0, max_workgroups=37)[0] == 37
+    gb = _launch_config(state_dtype="bf16")[0]
+    assert gb > 0 and gb % cus == 0
