@@ -111,6 +111,76 @@ def traffic_ratio(workload: str):
         return None
 
 
+def plain_alloc_run(steps: int):
+    """The headline call with torch's caching allocator (plain hipMalloc
+    pools) instead of the contiguous pools, measured in a child process that
+    runs before this one touches the GPU (so, on a fresh box, as the box's
+    first GPU process, where plain allocations drew the slowest memory)."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--plain-alloc", "--only-main",
+           "--steps", str(steps), "--warmup", "3"]
+    say("plain-allocation run in a child process:", " ".join(cmd[1:]))
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=600, cwd=ROOT)
+    except subprocess.TimeoutExpired:
+        return {"error": "timed out"}
+    for line in res.stderr.splitlines():
+        if line.startswith("[bench]"):
+            say("  child:", line[len("[bench] "):])
+    lines = [ln for ln in res.stdout.splitlines() if ln.startswith("{")]
+    if res.returncode != 0 or not lines:
+        return {"error": f"exit status {res.returncode}", "stderr_tail": res.stderr[-500:]}
+    r = json.loads(lines[-1])
+    return {"ms_per_call": r["ms_per_step"], "GB/s": r["value"], "frac_of_hbm_peak": r["roofline"]["frac"],
+            "steps": r["steps"], "pools": r["config"]["pools"],
+            "note": "same workload and kernel; the pools from torch's caching allocator (hipMalloc) in a child "
+                    "process run first. The headline uses physically contiguous pools (rssm_pool.h)"}
+
+
+def sweep_point(dp, tabs, spec, dev, stream, n: int, reps: int):
+    """(ms per call, mean algorithmic bytes) of calls with the first n entries
+    of a seeded permutation of the requests active, the set rotated over up
+    to 32 disjoint sets so that the 256 MB last-level cache cannot serve a
+    repeated request."""
+    import torch
+    import rssm_harness as hx
+    import rssm_inputs as ri
+    perm = np.random.default_rng(SEED).permutation(spec.B).astype(np.int32)
+
+    def active_list(ids):
+        a = np.full(spec.B, -1, np.int32)
+        a[:len(ids)] = ids
+        return torch.from_numpy(a).to(dev)
+    n_sets = 1 if n in (0, spec.B) else min(32, spec.B // n)
+    ids_sets = [perm[(j * n) % spec.B:(j * n) % spec.B + n] for j in range(n_sets)]
+    # one prepared call per set: the timed loop makes one C call per step
+    calls_n = [hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "active_request_indices": active_list(ids)}))
+               for ids in ids_sets]
+    it = [0]
+
+    def rot():
+        calls_n[it[0] % n_sets]()
+        it[0] += 1
+    # as many untimed calls as timed ones first: right after a run of lighter
+    # calls (the empty ones) the first calls of a small batch run slower
+    for _ in range(reps):
+        rot()
+    torch.cuda.synchronize()
+    ms_n = timed_calls(rot, reps, stream)
+    bytes_n = 0
+    if n:
+        tot = 0
+        for ids in ids_sets:
+            act = np.array([int(v) for v in ids] + [-1] * (spec.B - n), np.int32)
+            tot += hx.algorithmic_bytes(spec, ri.Meta(**{**dp.meta.__dict__, "active": act}))
+        bytes_n = tot // n_sets
+    return ms_n, bytes_n
+
+
+# active-request counts of the sweep and the calls timed at each
+SWEEP = ((0, 1000), (1, 256), (16, 64), (256, 10))
+
+
 def timed_calls(fn, n, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -217,6 +287,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="profile mode: warmup + timed steps only")
     ap.add_argument("--empty-only", action="store_true", help="profile mode: 200 calls with no active request")
+    ap.add_argument("--active-only", type=int, default=None, metavar="N",
+                    help="profile mode: one point of the active-request sweep (N requests, rotated sets)")
     ap.add_argument("--all-pad-only", action="store_true",
                     help="profile mode: 200 calls with every request listed and every source the pad slot")
     ap.add_argument("--pmc-calibrate", action="store_true",
@@ -227,6 +299,8 @@ def main():
                          "checkpoints, gdn_large and ssu_large in --pmc-calibrate only")
     ap.add_argument("--only-gdn", action="store_true",
                     help="profile mode: the gated-delta-rule commit line only")
+    ap.add_argument("--no-plain-alloc-run", action="store_true",
+                    help="skip the child process that times the headline call with plain allocations")
     ap.add_argument("--plain-alloc", action="store_true",
                     help="plain hipMalloc pools (torch's caching allocator) instead of physically contiguous ones")
     ap.add_argument("--only-ssu", action="store_true",
@@ -259,6 +333,11 @@ def main():
               "single MI355X; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
+    default_run = not (args.plain_alloc or args.only_main or args.empty_only or args.all_pad_only
+                       or args.active_only is not None
+                       or args.pmc_calibrate or args.only_checkpoints or args.only_gdn or args.only_ssu)
+    plain = plain_alloc_run(args.steps) if default_run and not args.no_plain_alloc_run else None
+
     import torch
     import rssm_harness as hx
     import rssm_inputs as ri
@@ -280,7 +359,7 @@ def main():
         print(json.dumps({"ssu_decode": ssu_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
         return
     profile_mode = (args.only_main or args.empty_only or args.all_pad_only or args.pmc_calibrate
-                    or args.only_checkpoints)
+                    or args.only_checkpoints or args.active_only is not None)
     wl = args.workload if profile_mode else WORKLOAD
     if wl == "checkpoints":
         wl = "large_bf16"   # the two-checkpoint call runs on the large_bf16 problem
@@ -302,6 +381,20 @@ def main():
 
     if args.only_checkpoints:
         print(json.dumps({"checkpoints": checkpoint_workload(dp, tabs, spec, stream, args.steps)}), flush=True)
+        return
+
+    if args.active_only is not None:
+        n = args.active_only
+        if not 0 <= n <= spec.B:
+            raise SystemExit(f"--active-only must be in [0, {spec.B}]")
+        reps = dict(SWEEP).get(n, 64)
+        ms_n, bytes_n = sweep_point(dp, tabs, spec, dev, stream, n, reps)
+        out = {"workload": wl, "active": n, "untimed_calls": reps, "timed_calls": reps,
+               "ms_per_call": round(ms_n, 5), "algorithmic_bytes": bytes_n}
+        if n:
+            out["GB/s"] = round(bytes_n / (ms_n * 1e-3) / 1e9, 1)
+        say(f"active={n}: {out}")
+        print(json.dumps(out), flush=True)
         return
 
     if args.empty_only or args.all_pad_only or args.pmc_calibrate:
@@ -355,6 +448,8 @@ def main():
         "us_per_request_full": round(ms * 1e3 / spec.B, 3),
         "single_call_ms_min_med_max": [round(singles[0], 3), round(singles[2], 3), round(singles[-1], 3)],
     }
+    if plain is not None:
+        result["plain_alloc"] = plain
     if args.only_main:
         print(json.dumps(result), flush=True)
         return
@@ -381,43 +476,10 @@ def main():
     say(f"ceilings: {result['ceilings']}")
 
     if not args.no_sweep:
-        rng = np.random.default_rng(SEED)
-        perm = rng.permutation(spec.B).astype(np.int32)
-
-        def active_list(ids):
-            a = np.full(spec.B, -1, np.int32)
-            a[:len(ids)] = ids
-            return torch.from_numpy(a).to(dev)
-
         sweep = {}
         t_empty = None
-        for n, reps in ((0, 1000), (1, 256), (16, 64), (256, max(4, args.steps // 2))):
-            # rotate the active set so the 256 MB last-level cache cannot serve it
-            n_sets = 1 if n in (0, 256) else min(32, spec.B // n)
-            sets = [active_list(perm[(j * n) % spec.B:(j * n) % spec.B + n]) for j in range(n_sets)]
-            # one prepared call per set: the timed loop makes one C call per step
-            calls_n = [hx.prepared(dp, hx.Tables(**{**tabs.__dict__, "active_request_indices": a_}))
-                       for a_ in sets]
-            it = [0]
-
-            def rot():
-                calls_n[it[0] % n_sets]()
-                it[0] += 1
-            for _ in range(3):
-                rot()
-            torch.cuda.synchronize()
-            ms_n = timed_calls(rot, reps, stream)
-            ids = [int(v) for v in sets[0].cpu().numpy()[:n]]
-            meta_n = dp.meta
-            bytes_n = hx.algorithmic_bytes(spec, ri.Meta(**{**meta_n.__dict__, "active": np.array(
-                ids + [-1] * (spec.B - n), np.int32)})) if n else 0
-            if n_sets > 1:  # mean over the rotated sets
-                tot = 0
-                for sset in sets:
-                    ids_s = [int(v) for v in sset.cpu().numpy()[:n]]
-                    tot += hx.algorithmic_bytes(spec, ri.Meta(**{**meta_n.__dict__, "active": np.array(
-                        ids_s + [-1] * (spec.B - n), np.int32)}))
-                bytes_n = tot // n_sets
+        for n, reps in SWEEP:
+            ms_n, bytes_n = sweep_point(dp, tabs, spec, dev, stream, n, reps)
             if n == 0:
                 t_empty = ms_n
             entry = {"ms_per_call": round(ms_n, 5), "algorithmic_bytes": bytes_n}
@@ -432,7 +494,7 @@ def main():
         result["empty_launch_us"] = round(t_empty * 1e3, 3)
 
         # empty launch under graph replay (100 captured calls)
-        empty = active_list([])
+        empty = torch.full((spec.B,), -1, dtype=torch.int32, device=dev)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())

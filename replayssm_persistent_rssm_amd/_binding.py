@@ -283,14 +283,18 @@ class MaterializeCall:
     once, and each call is one C call with the stored descriptor and tables.
 
     Same arguments as the entry point; stream=None binds torch's current
-    stream at construction.  The caller keeps every tensor alive while the
-    object is used.  A call may pass another device int32 tensor of shape
-    (B,) as the active list."""
+    stream at construction.  The object holds references to every argument
+    (the tables store only device addresses), so their memory stays
+    allocated while it lives.  A call may pass another device int32 tensor
+    of shape (B,) as the active list; it is held until the next call that
+    passes one."""
 
     def __init__(self, *args, stream=None, checkpoints: bool = False, **kw):
         self._ncp = None
         if checkpoints:
             self._ncp = _num_checkpoints(args[12] if len(args) > 12 else kw["dst_slots"])
+        self._keep = (args, kw)
+        self._active = None
         self._desc, self._tab = _marshal(*args, num_checkpoints=self._ncp, **kw)
         self._desc_ref = ctypes.byref(self._desc)
         self._tab_ref = ctypes.byref(self._tab)
@@ -308,6 +312,7 @@ class MaterializeCall:
             import torch
             self._tab.active_request_indices = _ptr(active_request_indices, "active_request_indices",
                                                     torch.int32, (self._batch,))
+            self._active = active_request_indices
         st = self._call()
         if st != RSSM_OK:
             raise RssmError(st, rssm_last_error())
@@ -363,9 +368,12 @@ gated_delta_rule_replayssm_commit = rssm_gdn_commit
 
 class GdnCommitCall:
     """A prepared rssm_gdn_commit: arguments checked and marshalled once; each
-    call is one C call.  stream=None binds torch's current stream."""
+    call is one C call.  stream=None binds torch's current stream.  The
+    object holds references to every argument (the tables store only device
+    addresses), so their memory stays allocated while it lives."""
 
     def __init__(self, *args, stream=None, **kw):
+        self._keep = (args, kw)
         self._desc, self._tab = _gdn_marshal(*args, **kw)
         self._refs = (ctypes.byref(self._desc), ctypes.byref(self._tab))
         self._stream = _stream_handle(stream)
@@ -431,9 +439,12 @@ def rssm_ssu_decode(*args, stream=None, **kw) -> None:
 
 class SsuDecodeCall:
     """A prepared rssm_ssu_decode: arguments checked and marshalled once; each
-    call is one C call.  stream=None binds torch's current stream."""
+    call is one C call.  stream=None binds torch's current stream.  The
+    object holds references to every argument (the tables store only device
+    addresses), so their memory stays allocated while it lives."""
 
     def __init__(self, *args, stream=None, **kw):
+        self._keep = (args, kw)
         self._desc, self._tab = _ssu_marshal(*args, **kw)
         self._refs = (ctypes.byref(self._desc), ctypes.byref(self._tab))
         self._stream = _stream_handle(stream)
