@@ -684,10 +684,11 @@ __device__ __forceinline__ void mfma_fold_heads(const KernelArgs& a, int lane, f
     }
     const int hb = max(h0, g * a.hpg);
     const int he = min(h1, (g + 1) * a.hpg);
-    // Each head's x rows, dt and A are requested one head ahead (right after
-    // the previous head has staged its own), and its first two row blocks
-    // during the previous head's last two: a head starts with its inputs
-    // arrived or in flight.
+    // By default each head requests its first two row blocks, x rows, dt and
+    // A at its start.  With PF (a tuning variant, off: on MI355X it ran the
+    // int8 workload 1% slower) the x rows, dt and A come one head ahead
+    // (right after the previous head has staged its own) and the first two
+    // row blocks during the previous head's last two.
     Chunk<IT> xraw[XREP];
     float A_n = 0.0f, dt_n = 0.0f;
     auto issue_small = [&](int hn) __attribute__((always_inline)) {
