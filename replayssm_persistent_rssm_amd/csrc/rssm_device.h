@@ -356,6 +356,16 @@ __device__ __forceinline__ uint32_t i8_round(float t, bool stochastic, uint32_t 
   return static_cast<uint32_t>(q) & 0xFFu;
 }
 
+// (a ^ b) + c as one gfx950 v_xad_u32 (checked on MI355X against the
+// two-instruction form); the compiler does not form it from the expression
+// (it emits a not, a shift and an add for the stochastic-rounding carry).
+// b is wave-uniform (a constant here).
+__device__ __forceinline__ uint32_t xor_add(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+  return r;
+}
+
 // Stochastic e4m3 rounding of a row-scaled value t with 2^-6 <= |t| (and t
 // not NaN; callers check the range for the whole wave first), returned as
 // the exactly representable fp32 value the code stands for.  |t| is first
@@ -368,7 +378,7 @@ __device__ __forceinline__ uint32_t i8_round(float t, bool stochastic, uint32_t 
 // bit is never reached: the clamped magnitude's bits are below 2^30.
 __device__ __forceinline__ float e4m3_sr_normal_value(float t, uint32_t u) {
   const float c = __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
-  const uint32_t x = __float_as_uint(c) + ((u >> 12) ^ 0xFFFFFu);
+  const uint32_t x = xor_add(u >> 12, 0xFFFFFu, __float_as_uint(c));
   return __uint_as_float(x & 0xFFF00000u);
 }
 
