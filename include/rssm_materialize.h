@@ -65,10 +65,11 @@ typedef enum {
  *   state_dtype      RSSM_F32 | RSSM_BF16 | RSSM_F16 | RSSM_I8 | RSSM_F8E4M3
  *   input_dtype      x and B ring dtype: RSSM_F32 | RSSM_BF16 | RSSM_F16
  *   a_dtype          A dtype: RSSM_F32 (dt is always fp32)
- *   max_workgroups   0: the default grid (the resident capacity; a multiple
- *                    of it for one-byte state, see rssm_materialize_launch_config;
- *                    the work loop is persistent); > 0: exactly this many
- *                    workgroups (results do not depend on it) */
+ *   max_workgroups   0: the default grid (the resident capacity; eight times
+ *                    it for one-byte state with stochastic rounding, see
+ *                    rssm_materialize_launch_config; the work loop is
+ *                    persistent); > 0: exactly this many workgroups (results
+ *                    do not depend on it) */
 typedef struct {
   int32_t num_layers;
   int32_t batch;
