@@ -358,16 +358,18 @@ __device__ __forceinline__ int ring_entry(int r0, int j, int R) {
 // gained 14%.  For int8 with 8-token windows, 4 rows in LDS ran 5% slower.
 template <int KMAX> constexpr int kBRegs = (KMAX > 8) ? 4 : KMAX;
 
-// int8 state, fp16 x/B, windows of up to 8, one checkpoint: B rows held as
-// packed fp16 pairs and multiplied with v_fma_mix_f32, which leaves room for
-// 5 waves per SIMD (4.3% faster than fp32 rows at 4 waves on MI355X; at 4
-// waves the packed rows alone ran 1% slower).
+// int8 state, fp16 x/B, windows of up to 8, one checkpoint, vector-ALU fold
+// (a tuning variant with the matrix-core fold off): B rows held as packed
+// fp16 pairs and multiplied with v_fma_mix_f32, which leaves room for 5 waves
+// per SIMD (4.3% faster than fp32 rows at 4 waves on MI355X; at 4 waves the
+// packed rows alone ran 1% slower).
 template <int ST, int IT, int KMAX, int NCK>
 constexpr bool kMixB = (ST == kI8 && IT == kF16 && KMAX <= 8 && NCK == 1);
 
 // Resident wavefronts per SIMD the register budget of the VALU fold is sized
 // for (two- and four-byte state, and every multi-checkpoint instance; the
-// one-byte single-checkpoint instances fold on the matrix cores at 4 waves).
+// one-byte single-checkpoint instances fold on the matrix cores at 4 waves,
+// and reach the one-byte rules below only with that fold switched off).
 // e4m3 state adds software decode/encode on top of the row scales: its
 // 8-token instances get a 3-wave budget (168 registers) so they do not spill.
 // int8 keeps 4 waves (5 with packed fp16 B rows, above).
