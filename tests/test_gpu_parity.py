@@ -105,6 +105,31 @@ def test_dtype_matrix(dev, state, inp, rounds):
     check(ri.make_problem(spec, 2000 + ri.DTYPE_CODE[state] * 10 + ri.DTYPE_CODE[inp]), dev)
 
 
+# More than 256 requests: the active-list scan pages through the list 256
+# entries at a time, and the kernel reads request indices past 255 from memory.
+BIG_BATCH = ri.Spec("big_batch", L=2, B=600, H=2, hpg=1, dim=64, dstate=128, R=8, W=8, k_lo=0, k_hi=8,
+                    slots=1300, slot_mode="perm", pad_frac=0.1, rand_seed=91)
+
+
+@pytest.mark.parametrize("state,inp,rounds,n_active", [
+    ("bf16", "bf16", 0, 256), ("bf16", "bf16", 0, 257), ("bf16", "bf16", 0, 600),
+    ("i8", "f16", 0, 450), ("f8e4m3", "bf16", 10, 450)])
+def test_batch_over_256(dev, state, inp, rounds, n_active):
+    """600 requests (450 listed, or the list ending at 256 / 257 / not at all),
+    a tenth of the (layer, request) pairs padded; the default grid, and 8
+    workgroups, where every wavefront deals many chunks and filters their
+    liveness in batches.  One oracle result serves both launches."""
+    import oracle
+    import parity
+    spec = ri.with_(BIG_BATCH, state_dtype=state, input_dtype=inp, philox_rounds=rounds, n_active=n_active)
+    prob = ri.make_problem(spec, 2400 + n_active)
+    expected = oracle.materialize(prob, want_exact=True)
+    for mw in (0, 8):
+        say("big batch", state, inp, rounds, n_active, "max_workgroups", mw)
+        st, sc, _ = run_gpu(prob, dev, max_workgroups=mw)
+        parity.check_against_oracle(prob, st, sc, expected=expected)
+
+
 @pytest.mark.parametrize("state", ["f32", "bf16", "f16"])
 def test_small_tile_16x16(dev, state):
     spec = ri.with_(ri.CONFIGS["tiny_f32"], name="t16", L=2, B=5, H=6, hpg=3, state_dtype=state,
