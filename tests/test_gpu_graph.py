@@ -38,7 +38,7 @@ def _same(a, b):
 
 
 @pytest.mark.parametrize("state,rounds,checkpoints", [("bf16", 0, False), ("f8e4m3", 10, False),
-                                                      ("i8", 0, True)])
+                                                      ("i8", 0, False), ("i8", 0, True)])
 def test_graph_replays_match_eager(dev, state, rounds, checkpoints):
     import torch
     import rssm_harness as hx
