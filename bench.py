@@ -843,7 +843,7 @@ def counters_summary(fetch_csv, write_csv, alg_json):
     wr = sum(facs[1][2]) / len(facs[1][2]) * facs[1][3] * 1024
     repo = "$REPO"
     out.append(f"# HBM traffic of {COUNTER_DESCRIPTION[wl]}; one call per dispatch")
-    out.append("# commands (REPO = repository root on the GPU box):")
+    out.append("# commands (REPO = repository root on the MI355X machine):")
     for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         out.append(f"#   cd /tmp && rocprofv3 --pmc {c} --output-format csv -d /tmp/pmc_{d} -o {d} -- "
                    f"python3 {repo}/bench.py --pmc-calibrate --workload {wl} > /tmp/alg_{d}.json")
