@@ -12,9 +12,9 @@
  * on a box can land on physical memory that streams markedly slower than a
  * physically contiguous allocation: a 20 GiB device copy ran at 4.7 TB/s
  * against 5.7 TB/s, and the 48-layer bf16 materialize at 19.4 ms (67-68% of
- * the 8 TB/s HBM peak) against 17.2 ms (76-77%): the 70% roofline fraction
- * of that workload holds with contiguous pools, not with plain allocations
- * in a box's first process.  These entry points allocate with
+ * the 8 TB/s HBM peak) against 16.9-17.2 ms (76-78%): the 70% roofline
+ * fraction of that workload holds with contiguous pools, not with plain
+ * allocations in the first process on such a machine.  These entry points allocate with
  * hipDeviceMallocContiguous and
  * fall back to hipMalloc when the device has no contiguous range that large.
  *
