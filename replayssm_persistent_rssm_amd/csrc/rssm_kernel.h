@@ -441,8 +441,11 @@ __device__ __forceinline__ void sort_checkpoints(int (&kc)[NCK], int (&dc)[NCK])
 // instructions and the fold k fused multiply-adds, against about 9.8
 // instructions' worth of issue time per element at HBM speed.  The fold is
 // a rank-k update of the tile, U = W X^T B with k <= 16, i.e. a small dense
-// contraction: these instances run it as fp32 16x16x4 MFMAs, which execute
-// on the matrix cores beside the VALU work (Philox, row scales, encode).
+// contraction: these instances run it as fp32 16x16x4 MFMAs.  One MFMA does
+// 1024 multiply-adds in 32 cycles, twice the rate of unpacked vector FMAs,
+// and leaves the vector issue slots to Philox, row scales and encode; on
+// MI355X it does not overlap that work (the fp32 matrix rate equals the
+// fp32 vector rate), so the saving is the issue rate.
 //
 // Layout.  A tile is 4 blocks of 16 rows.  In a row block, lane L holds row
 // j = L % 16 and, with q = L / 16, the 32 columns [16q, 16q + 16) and
