@@ -329,8 +329,8 @@ def main():
         print(trace_summary(args.summarize_trace), end="")
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this path needs no collectives and every run here uses a "
-              "single MI355X; --gpus must be 1", file=sys.stderr)
+        print("bench.py measures one GPU: the path needs no collectives (each GPU would run the same kernel "
+              "on its own heads, requests or layers); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     default_run = not (args.plain_alloc or args.only_main or args.empty_only or args.all_pad_only
