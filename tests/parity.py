@@ -10,7 +10,14 @@ Tolerances (written here, per the method's arithmetic):
     one ulp finer than fp32 accumulation can resolve -- within
     1e-5 * M + half an ulp of the exact value;
   * int8 / e4m3 state: codes within one step in value order of the oracle's,
-    row scales within 1e-5 relative of the oracle's.
+    row scales within 1e-5 relative of the oracle's;
+  * NaN: the GPU's code is a NaN code of the format exactly where the
+    oracle's is, of either sign (and any payload).  IEEE 754 leaves the sign
+    and payload of a NaN that arithmetic produces unspecified, so only the
+    NaN-ness is unique.  int8 encodes NaN as 0, which is compared as a code;
+  * an infinite exact value (an infinity in the inputs) in fp32 / bf16 / fp16
+    state: the GPU's value is that same infinity (M is infinite there, so the
+    relative bound would accept anything).
 The fp32 accumulation error of the GPU fold is bounded by a few ulps of fp32
 times M (k <= 16 fused multiply-adds plus one exp per token), far inside
 1e-5 * M.
@@ -43,24 +50,50 @@ def ulp_at(dtype: str, v: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.maximum(e, emin) - mant)
 
 
+def nan_codes(dtype: str, codes: np.ndarray) -> np.ndarray:
+    """Per element: is the code a NaN of the format (any sign, any payload)?"""
+    c = np.asarray(codes)
+    if dtype == "i8":
+        return np.zeros(c.view(np.int8).shape, bool)
+    if dtype == "f8e4m3":
+        return (c.view(np.uint8) & 0x7F) == 0x7F
+    if dtype == "f32":
+        return np.isnan(c.view(np.float32))
+    exp_mask, mant_mask = {"bf16": (0x7F80, 0x007F), "f16": (0x7C00, 0x03FF)}[dtype]
+    u = c.view(np.uint16)
+    return ((u & exp_mask) == exp_mask) & ((u & mant_mask) != 0)
+
+
 def compare_tile(dtype: str, got, exp_codes, exact, mag, got_scale=None, exp_scale=None, what=""):
     """Compare one written region (k > 0) of codes (and row scales)."""
     got = np.asarray(got).reshape(-1)
     exp_codes = np.asarray(exp_codes).reshape(-1)
+    en, gn = nan_codes(dtype, exp_codes), nan_codes(dtype, got)
+    assert np.array_equal(gn, en), (f"{what}: NaN elements differ ({(en & ~gn).sum()} NaN in the oracle only, "
+                                    f"{(gn & ~en).sum()} on the GPU only)")
+    if en.any():
+        # the rest as usual; the NaN elements compare equal from here on
+        exact = np.where(en.reshape(np.shape(exact)), 0.0, exact)
+        mag = np.where(en.reshape(np.shape(mag)), 0.0, mag)
+        got, exp_codes = _zero_elements(dtype, got, en), _zero_elements(dtype, exp_codes, en)
     exact = np.asarray(exact, np.float64).reshape(-1)
     mag = np.asarray(mag, np.float64).reshape(-1)
     if dtype == "f32":
         g = got.view(np.float32).astype(np.float64)
-        err = np.abs(g - exact)
-        bad = ~(err <= 1e-5 * mag)
-        assert not bad.any(), (f"{what}: {bad.sum()} fp32 elements beyond 1e-5*M; worst "
-                               f"{(err / np.maximum(mag, 1e-300)).max():.3e}")
+        with np.errstate(invalid="ignore"):   # inf - inf where both hold the same infinity
+            err = np.abs(g - exact)
+        bad = ~((err <= 1e-5 * mag) | (g == exact)) | (np.isinf(exact) & (g != exact))
+        if bad.any():
+            with np.errstate(invalid="ignore"):
+                worst = (err / np.maximum(mag, 1e-300))[bad].max()
+            raise AssertionError(f"{what}: {bad.sum()} fp32 elements beyond 1e-5*M; worst {worst:.3e}")
         return
     di = np.abs(ordered_index(dtype, got) - ordered_index(dtype, exp_codes))
     if dtype in ("bf16", "f16"):
         g = oracle.decode(dtype, got.view(np.uint16)) if got.size <= 4096 else _fast_decode(dtype, got)
-        near = np.abs(g - exact) <= 1e-5 * mag + 0.5 * ulp_at(dtype, np.maximum(np.abs(g), np.abs(exact)))
-        bad = ~((di <= 1) | near)
+        with np.errstate(invalid="ignore"):   # inf - inf: not near, decided by the code step
+            near = np.abs(g - exact) <= 1e-5 * mag + 0.5 * ulp_at(dtype, np.maximum(np.abs(g), np.abs(exact)))
+        bad = ~((di <= 1) | near) | (np.isinf(exact) & (g != exact))
         assert not bad.any(), f"{what}: {bad.sum()} {dtype} codes off by more than 1 ulp (max {di.max()})"
         return
     bad = di > 1
@@ -70,6 +103,14 @@ def compare_tile(dtype: str, got, exp_codes, exact, mag, got_scale=None, exp_sca
         es = np.asarray(exp_scale, np.float64).reshape(-1)
         rel = np.abs(gs - es) / np.maximum(np.abs(es), 1e-300)
         assert np.all(rel <= 1e-5), f"{what}: row scales differ by up to {rel.max():.3e}"
+
+
+def _zero_elements(dtype: str, codes: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """A copy of the codes with the masked elements set to the code of +0."""
+    view = {"f8e4m3": np.uint8, "bf16": np.uint16, "f16": np.uint16, "f32": np.uint32}[dtype]
+    out = np.array(codes, copy=True)
+    out.view(view)[mask] = 0
+    return out
 
 
 def _fast_decode(dtype: str, codes: np.ndarray) -> np.ndarray:

@@ -47,13 +47,13 @@ def run_gpu(prob, dev, max_workgroups=0, active=None):
     return st, sc, ring
 
 
-def check(prob, dev, **kw):
+def check(prob, dev, expected=None, **kw):
     import parity
     st, sc, ring = run_gpu(prob, dev, **kw)
     for got, want in zip(ring, [prob.x, prob.Bm, prob.dt, prob.A]):
         for g, w in zip(got, want):
             assert np.array_equal(g.view(np.uint8), w.view(np.uint8)), "ring or A changed"
-    parity.check_against_oracle(prob, st, sc)
+    parity.check_against_oracle(prob, st, sc, expected)
     return st, sc
 
 
@@ -310,6 +310,116 @@ def test_rounding_bit_exact_on_exact_inputs(dev, state, rounds, window, inp):
             pytest.fail(f"layer {l}: {int((g != o).sum())} bytes differ; first: " + "; ".join(lines))
         if sc is not None:
             assert np.array_equal(sc[l].view(np.uint32), sc_o[l].view(np.uint32)), f"layer {l} scales differ"
+
+
+@pytest.mark.parametrize("state,rounds", [("i8", 0), ("i8", 10), ("f8e4m3", 0), ("f8e4m3", 10)])
+@pytest.mark.parametrize("window", [8, 16])
+def test_one_byte_special_rows(dev, state, rounds, window):
+    """Rows the one-byte encode treats specially, through the whole kernel (the
+    matrix-core fold's row-block encode), in every written source slot: an
+    all-zero row (zero codes and x entries: scale 0, zero codes), a row whose
+    huge source scale overflows to infinity (scale 0, zero codes) and, for
+    e4m3, a NaN source code inside an otherwise normal row (the NaN code of
+    either sign at that element, the row's other codes and scale unchanged by
+    it)."""
+    spec = ri.with_(MATRIX, state_dtype=state, input_dtype="bf16", philox_rounds=rounds, rand_seed=4321,
+                    W=window, k_lo=1, k_hi=window, R=window + 3, hpg=2 if window > 8 else MATRIX.hpg)
+    prob = ri.make_problem(spec, 2700 + window)
+    m, H, dim, ds = prob.meta, spec.H, spec.dim, spec.dstate
+    zero_hr, inf_hr, nan_hrc = (0, 3), (1, 5), (2, 9, 7)
+    for l in range(spec.L):
+        prob.A[l][inf_hr[0]] = 0.0   # no decay: code x 1e38 overflows whatever the prefix
+        for b in range(spec.B):
+            s_ = int(m.src[l, b])
+            if s_ == spec.pad_slot_id:
+                continue
+            st = prob.state[l][s_]
+            h, r = zero_hr
+            st[(h * dim + r) * ds:(h * dim + r + 1) * ds] = 0
+            for e in range(spec.R):
+                prob.x[l][s_, (e * H + h) * dim + r] = 0
+            h, r = inf_hr
+            prob.scale[l][s_, h * dim + r] = 1e38
+            st[(h * dim + r) * ds:(h * dim + r) * ds + 8] = 0x7E if state == "f8e4m3" else 100
+            if state == "f8e4m3":
+                h, r, c = nan_hrc
+                st[(h * dim + r) * ds + c] = 0x7F
+    say("special rows", state, rounds, "window", window)
+    expected = oracle_result(prob)
+    st_g, sc_g = check(prob, dev, expected)
+    st_o, sc_o = expected[0], expected[1]
+    # the special rows of every written destination, exactly
+    for l in range(spec.L):
+        for i in range(spec.B):
+            b = int(m.active[i])
+            if b < 0:
+                break
+            s_, d_ = int(m.src[l, b]), int(m.dst[l, b])
+            if s_ == spec.pad_slot_id or d_ == spec.pad_slot_id or int(m.prefix[b]) == 0:
+                continue
+            for (h, r) in (zero_hr, inf_hr):
+                row = slice((h * dim + r) * ds, (h * dim + r + 1) * ds)
+                assert not st_g[l][d_, row].any(), f"layer {l} slot {d_} head {h} row {r}: codes not zero"
+                assert sc_g[l][d_, h * dim + r] == 0.0, f"layer {l} slot {d_} head {h} row {r}: scale not 0"
+            if state == "f8e4m3":
+                # the NaN row: the other codes as the oracle's (its scale is
+                # compared within 1e-5 above), the NaN element a NaN code
+                # (its sign is not fixed, IEEE 754)
+                h, r, c = nan_hrc
+                at = (h * dim + r) * ds + c
+                row = np.r_[(h * dim + r) * ds:at, at + 1:(h * dim + r + 1) * ds]
+                assert np.array_equal(st_g[l][d_, row], st_o[l][d_, row]), f"layer {l} slot {d_}: NaN row differs"
+                assert st_o[l][d_, at] == 0x7F and st_g[l][d_, at] & 0x7F == 0x7F
+
+
+@pytest.mark.parametrize("state", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("window", [8, 16])
+def test_wide_state_special_values(dev, state, window):
+    """NaN and infinities in a source state of a wide dtype, through the whole
+    kernel: the NaN element stays NaN (of either sign: IEEE 754 does not fix
+    the sign of a NaN that arithmetic yields), each infinity stays the same
+    infinity (the decay is positive and the added terms finite), and every
+    other element is compared with the oracle as usual."""
+    spec = ri.with_(MATRIX, state_dtype=state, input_dtype="bf16", W=window, k_lo=1, k_hi=window, R=window + 3,
+                    hpg=2 if window > 8 else MATRIX.hpg)
+    prob = ri.make_problem(spec, 2800 + window)
+    m, dim, ds = prob.meta, spec.dim, spec.dstate
+    nan, pinf, ninf = {"f32": (np.float32(np.nan), np.float32(np.inf), np.float32(-np.inf)),
+                       "bf16": (0x7FC0, 0x7F80, 0xFF80),
+                       "f16": (np.float16(np.nan), np.float16(np.inf), np.float16(-np.inf))}[state]
+    spots = [((2, 9, 7), nan), ((1, 5, 3), pinf), ((1, 5, 4), ninf), ((7, 63, 127), pinf)]
+    for l in range(spec.L):
+        for b in range(spec.B):
+            s_ = int(m.src[l, b])
+            if s_ == spec.pad_slot_id:
+                continue
+            for (h, r, c), v in spots:
+                prob.state[l][s_, (h * dim + r) * ds + c] = v
+    say("wide special values", state, "window", window)
+    expected = oracle_result(prob)
+    st_g, _ = check(prob, dev, expected)
+    st_o = expected[0]
+    n_checked = 0
+    for l in range(spec.L):
+        for i in range(spec.B):
+            b = int(m.active[i])
+            if b < 0:
+                break
+            s_, d_ = int(m.src[l, b]), int(m.dst[l, b])
+            if s_ == spec.pad_slot_id or d_ == spec.pad_slot_id or int(m.prefix[b]) == 0:
+                continue
+            for (h, r, c), v in spots[1:]:
+                at = (h * dim + r) * ds + c
+                assert st_o[l][d_, at].tobytes() == np.asarray(v, st_o[l].dtype).tobytes()
+                assert st_g[l][d_, at].tobytes() == st_o[l][d_, at].tobytes(), \
+                    f"layer {l} slot {d_} head {h} row {r} col {c}: infinity not kept"
+            n_checked += 1
+    assert n_checked > 0
+
+
+def oracle_result(prob):
+    import oracle
+    return oracle.materialize(prob, want_exact=True)
 
 
 @pytest.mark.parametrize("state", ["bf16", "f16", "i8", "f8e4m3"])
