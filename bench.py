@@ -318,9 +318,16 @@ def main():
                     help="print the kernel-stats table of a --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
                     help="print the counter values of each materialize dispatch of a --pmc run and exit")
+    ap.add_argument("--summarize-valu", nargs=2, metavar=("COUNTER_CSV", "BENCH_JSON"),
+                    help="print the vector-ALU table row of a --pmc run of SQ_ACTIVE_INST_VALU, GRBM_GUI_ACTIVE, "
+                         "SQ_INSTS_VALU and SQ_WAVES over --only-main/--only-gdn/--only-ssu (and the JSON line "
+                         "that run printed) and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(pmc_summary(args.summarize_pmc), end="")
+        return
+    if args.summarize_valu:
+        print(valu_summary(*args.summarize_valu), end="")
         return
     if args.summarize_counters:
         print(counters_summary(*args.summarize_counters), end="")
@@ -353,10 +360,14 @@ def main():
     if args.workload in ("gdn_large", "ssu_large", "checkpoints") and not args.pmc_calibrate:
         raise SystemExit(f"--workload {args.workload} is a counter-mode workload (--pmc-calibrate)")
     if args.only_gdn:
-        print(json.dumps({"gdn_commit": gdn_workload(dev, torch.cuda.current_stream(), args.steps, with_null=False)}), flush=True)
+        out = gdn_workload(dev, torch.cuda.current_stream(), args.steps, with_null=False)
+        print(json.dumps({"gdn_commit": out, "valu_workload": "gdn_large", "valu_kernel": "gdn_commit_kernel",
+                          "valu_elements": out["state_element_tokens"]}), flush=True)
         return
     if args.only_ssu:
-        print(json.dumps({"ssu_decode": ssu_workload(dev, torch.cuda.current_stream(), args.steps)}), flush=True)
+        out = ssu_workload(dev, torch.cuda.current_stream(), args.steps)
+        print(json.dumps({"ssu_decode": out, "valu_workload": "ssu_large", "valu_kernel": "ssu_decode_kernel",
+                          "valu_elements": out["checkpoint_elements"]}), flush=True)
         return
     profile_mode = (args.only_main or args.empty_only or args.all_pad_only or args.pmc_calibrate
                     or args.only_checkpoints or args.active_only is not None)
@@ -451,6 +462,8 @@ def main():
     if plain is not None:
         result["plain_alloc"] = plain
     if args.only_main:
+        result.update(valu_workload=wl, valu_kernel="materialize_kernel",
+                      valu_elements=written_state_elements(spec, dp.meta))
         print(json.dumps(result), flush=True)
         return
 
@@ -650,7 +663,11 @@ def gdn_workload(dev, stream, steps, with_null: bool = True):
            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "us_per_request": round(ms * 1e3 / max(live, 1), 3),
-           "traffic_over_algorithmic": traffic_ratio("gdn_large")}
+           "traffic_over_algorithmic": traffic_ratio("gdn_large"),
+           # state elements times the tokens each commits (the vector-ALU table's denominator)
+           "state_element_tokens": sum(spec.L * spec.HV * spec.dv * spec.dk * min(int(dp.accept_lens[b]), spec.T)
+                                       for b in range(spec.B)
+                                       if dp.state_indices[b] > spec.null_block_id and dp.accept_lens[b] > 0)}
     # every request null: the work discovery alone (nothing is written); left
     # out in the profile mode, whose trace then holds only the full calls
     if not with_null:
@@ -702,7 +719,8 @@ def ssu_workload(dev, stream, steps):
            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "us_per_request": round(ms * 1e3 / max(live, 1), 3),
-           "traffic_over_algorithmic": traffic_ratio("ssu_large")}
+           "traffic_over_algorithmic": traffic_ratio("ssu_large"),
+           "checkpoint_elements": live * spec.H * spec.dim * spec.dstate}
     say(f"ssu_decode: {out}")
     del call, dp
     torch.cuda.empty_cache()
@@ -865,6 +883,47 @@ def counters_summary(fetch_csv, write_csv, alg_json):
     out.append(f"algorithmic_bytes_per_launch: {alg}")
     out.append(f"traffic_over_algorithmic: {(rd + wr) / alg:.4f}")
     return "\n".join(out) + "\n"
+
+
+def written_state_elements(spec, meta) -> int:
+    """State elements one materialize call writes: every listed request's
+    (layer) pairs whose source and destination are not the pad slot."""
+    n = 0
+    for b in meta.active:
+        if b < 0 or b >= spec.B:
+            break
+        n += int(((meta.src[:, b] != spec.pad_slot_id) & (meta.dst[:, b] != spec.pad_slot_id)).sum())
+    return n * spec.H * spec.dim * spec.dstate
+
+
+VALU_HEADER = ("# workload | kernel | SQ_WAVES | SQ_INSTS_VALU | SQ_ACTIVE_INST_VALU | GRBM_GUI_ACTIVE | valu_time_ms | "
+               "elements | VALU instr/element")
+
+
+def valu_summary(counter_csv, bench_json):
+    """One row of the vector-ALU table from a --pmc run of SQ_ACTIVE_INST_VALU,
+    GRBM_GUI_ACTIVE, SQ_INSTS_VALU and SQ_WAVES over a profile-mode bench run,
+    and the JSON line that run printed (its `valu_elements` is the per-element
+    denominator).  Every dispatch of the workload reads alike; the last one is
+    used.  valu_time_ms = SQ_INSTS_VALU * 4 cycles (a wave64 instruction on a
+    16-lane SIMD) / 1024 SIMDs / 2.4 GHz, a lower bound on vector issue time
+    (matrix-core instructions are counted as one instruction each)."""
+    info = None
+    for line in open(bench_json):
+        line = line.strip()
+        if line.startswith("{") and "valu_elements" in line:
+            info = json.loads(line)
+    if info is None:
+        raise SystemExit(f"{bench_json}: no JSON line with valu_elements")
+    lines = [ln for ln in pmc_summary(counter_csv).splitlines() if info["valu_kernel"] in ln]
+    if not lines:
+        raise SystemExit(f"{counter_csv}: no {info['valu_kernel']} dispatch")
+    vals = dict(kv.split("=") for kv in lines[-1].split(": ", 1)[1].split())
+    ins = float(vals["SQ_INSTS_VALU"])
+    elems = int(info["valu_elements"])
+    return (f"{info['valu_workload']} | {info['valu_kernel']} | {float(vals['SQ_WAVES']):.0f} | {ins:.4e} | "
+            f"{float(vals['SQ_ACTIVE_INST_VALU']):.4e} | {float(vals['GRBM_GUI_ACTIVE']):.4e} | "
+            f"{ins * 4 / 1024 / 2.4e9 * 1e3:.3f} | {elems} | {ins * 64 / elems:.2f}\n")
 
 
 def pmc_summary(path):

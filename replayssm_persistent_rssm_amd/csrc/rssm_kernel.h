@@ -1276,6 +1276,12 @@ __global__ void __launch_bounds__(kBlock, (waves_per_simd<Tune, KMAX, ST, IT, NC
 
         // Stream the tile: decode, fold the prefix, encode, store.  Passes go
         // in groups of PD; while a group is folded the next group is in flight.
+        // (In the gfx950 code the buffers are copied at the loop's back edge,
+        // and the copies wait for every outstanding memory operation, so about
+        // one pass stays in flight.  Reloading each buffer only after it is
+        // consumed, with exact waits, kept two in flight but ran the full
+        // batch 2% slower on MI355X: sixteen wavefronts per CU saturate HBM
+        // either way, and the extra outstanding traffic cost efficiency.)
 #pragma unroll 1
         for (int p0 = 0; p0 < NPASS; p0 += PD) {
 #pragma unroll

@@ -49,10 +49,24 @@ def test_counter_summary_from_other_code_gives_no_traffic(tmp_path, monkeypatch)
     assert bench.traffic_from_profile("large_bf16") is None
 
 
-def test_committed_counter_summary_is_stale_for_current_kernel():
-    """The committed large_bf16 counter summary predates the current kernel
-    source, so the bench line must report no traffic figure from it."""
-    assert bench.traffic_from_profile("large_bf16") is None
+@pytest.mark.parametrize("workload", sorted(bench.COUNTER_FILE))
+def test_committed_counter_summaries_follow_the_hash_rule(workload):
+    """Each committed counter summary gives a traffic figure exactly when it
+    was taken on the current kernel source; such a figure is the algorithmic
+    bytes plus at most a few percent (re-reads, partial lines)."""
+    path = os.path.join(ROOT, "profiles", bench.COUNTER_FILE[workload])
+    assert os.path.exists(path), path
+    lines = [ln for ln in open(path) if ln.startswith("kernel_source_hash:")]
+    assert len(lines) == 1
+    current = lines[0].split(":", 1)[1].strip() == bench.kernel_hash(bench.COUNTER_SOURCES[workload])
+    ratio = bench.traffic_ratio(workload)
+    if not current:
+        assert ratio is None and bench.traffic_from_profile(workload) is None
+        return
+    assert 1.0 <= ratio < 1.1
+    vals = bench.counter_values(workload)
+    assert float(vals["hbm_bytes_per_launch"]) == pytest.approx(ratio * float(vals["algorithmic_bytes_per_launch"]),
+                                                                rel=1e-3)
 
 
 def test_trace_summary_format(tmp_path):
@@ -70,3 +84,26 @@ def test_more_than_one_gpu_is_refused():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_valu_summary_row(tmp_path):
+    """The vector-ALU row: the last dispatch of the named kernel, its counters,
+    valu_time = instructions x 4 cycles / 1024 SIMDs / 2.4 GHz, and
+    instructions x 64 lanes / elements."""
+    csv = tmp_path / "valu_counter_collection.csv"
+    rows = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"']
+    for d, ins in ((1, 100.0), (2, 2.4e9)):
+        for c, v in (("SQ_INSTS_VALU", ins), ("SQ_ACTIVE_INST_VALU", ins * 1.01), ("SQ_WAVES", 4096.0),
+                     ("GRBM_GUI_ACTIVE", 4.0e7)):
+            rows.append(f'{d},"void rssm::materialize_kernel<1>(rssm::KernelArgs)","{c}",{v}')
+    rows.append('3,"__amd_rocclr_copyBuffer","SQ_INSTS_VALU",5')
+    csv.write_text("\n".join(rows) + "\n")
+    js = tmp_path / "bench.json"
+    js.write_text('[bench] a log line\n{"valu_workload": "large_bf16", "valu_kernel": "materialize_kernel", '
+                  '"valu_elements": 1600000000}\n')
+    cells = [c.strip() for c in bench.valu_summary(str(csv), str(js)).split("|")]
+    assert cells[0] == "large_bf16" and cells[1] == "materialize_kernel" and cells[2] == "4096"
+    assert float(cells[3]) == pytest.approx(2.4e9)
+    assert float(cells[6]) == pytest.approx(2.4e9 * 4 / 1024 / 2.4e9 * 1e3, rel=1e-3)
+    assert int(cells[7]) == 1600000000
+    assert float(cells[8]) == pytest.approx(2.4e9 * 64 / 1.6e9, abs=0.01)
