@@ -88,6 +88,7 @@ def test_small_workload(dev, seed):
     dict(T=16, HV=3, H=3, accept=[16, 9, 0, 1, 15, 16]),
     dict(T=3, HV=8, H=1),
     dict(T=5, accept=[5, 5, 5, 5, 5, 5], zero_frac=0.0, null_frac=0.0),
+    dict(L=80, HV=2, H=1),   # more layers than a wavefront has lanes
 ])
 def test_variants(dev, kw):
     spec = ri.with_(ri.GDN_CONFIGS["gdn_small"], **kw)

@@ -208,6 +208,23 @@ def test_all_listed_all_pad_many_chunks(dev):
         check(prob, dev, max_workgroups=mw)
 
 
+@pytest.mark.parametrize("state,inp,dim,dstate,rounds", [("bf16", "bf16", 16, 16, 0), ("f32", "f16", 16, 16, 0),
+                                                         ("i8", "f16", 64, 128, 0), ("f8e4m3", "bf16", 64, 128, 10)])
+def test_more_layers_than_a_wavefront(dev, state, inp, dim, dstate, rounds):
+    """80 layers (more than one wavefront's 64 lanes) with padded pairs mixed
+    in: every per-layer table is read at indices past 63, chunks straddle
+    (request, layer) pairs (H = 6), and the one-byte cases run the
+    matrix-core fold."""
+    spec = ri.with_(MATRIX, L=80, B=3, H=6 if dim == 16 else 2, hpg=3 if dim == 16 else 1, dim=dim, dstate=dstate,
+                    state_dtype=state, input_dtype=inp, philox_rounds=rounds, slots=6, ring_slots=6,
+                    pad_frac=0.2, stride_pad="per_layer")
+    prob = ri.make_problem(spec, 2330 + dim + rounds)
+    expected = oracle_result(prob)
+    for mw in (0, 5):
+        say("80 layers", state, inp, f"{dim}x{dstate}", "rounds", rounds, "grid", mw)
+        check(prob, dev, expected, max_workgroups=mw)
+
+
 def test_entries_after_first_terminator_ignored(dev):
     prob = ri.make_problem(ri.with_(MATRIX, n_active=3), 2303)
     prob.meta.active[1] = -1                  # only the first request counts
