@@ -225,6 +225,46 @@ def test_more_layers_than_a_wavefront(dev, state, inp, dim, dstate, rounds):
         check(prob, dev, expected, max_workgroups=mw)
 
 
+@pytest.mark.parametrize("state,inp", [("bf16", "bf16"), ("i8", "f16")])
+def test_out_of_range_metadata_guards(dev, state, inp):
+    """Device metadata outside its documented range is undefined on the
+    pages; the kernel guards against faults instead: k is clamped to
+    [0, max_window], ring_start is taken modulo R, a negative source or
+    destination slot skips its (layer, request), and an active entry outside
+    [0, B) ends the list.  The result must equal the oracle's on metadata
+    sanitised that way (the oracle itself rejects such values)."""
+    import copy
+    import parity
+    spec = ri.with_(MATRIX, B=6, slots=12, ring_slots=12, state_dtype=state, input_dtype=inp)
+    bad = ri.make_problem(spec, 2340)
+    m, W, R, pad = bad.meta, spec.W, spec.R, spec.pad_slot_id
+    act = [int(v) for v in m.active[:5]]
+    assert len(set(act)) == 5 and min(act) >= 0
+    m.prefix[act[0]] = W + 9                  # clamped to W
+    m.prefix[act[1]] = -4                     # clamped to 0: a copy
+    m.ring_start[act[2]] = -11                # taken modulo R
+    m.ring_start[act[3]] = 3 * R + 5
+    m.src[0, act[0]] = -5                     # negative slots (not the pad id): skipped
+    m.dst[1, act[1]] = -9
+    m.active[4] = spec.B + 3                  # out of range: ends the list
+    m.active[5] = act[4]                      # after the end: ignored
+    sane = copy.copy(bad)
+    sane.meta = copy.deepcopy(m)
+    sm = sane.meta
+    sm.active[4:] = -1
+    sm.prefix[:] = np.clip(sm.prefix, 0, W)
+    sm.ring_start[:] = np.mod(sm.ring_start, R)
+    neg = (sm.src < 0) & (sm.src != pad) | (sm.dst < 0) & (sm.dst != pad)
+    sm.src[neg] = pad
+    sm.dst[neg] = pad
+    say("out-of-range metadata", state, inp)
+    st, sc, ring = run_gpu(bad, dev)
+    for got, want in zip(ring, [bad.x, bad.Bm, bad.dt, bad.A]):
+        for g, w in zip(got, want):
+            assert np.array_equal(g.view(np.uint8), w.view(np.uint8)), "ring or A changed"
+    parity.check_against_oracle(sane, st, sc)
+
+
 def test_entries_after_first_terminator_ignored(dev):
     prob = ri.make_problem(ri.with_(MATRIX, n_active=3), 2303)
     prob.meta.active[1] = -1                  # only the first request counts
