@@ -101,6 +101,35 @@ def test_variants(dev, kw):
     check(prob, run(prob, dev), str(kw))
 
 
+def test_out_of_range_metadata_guards(dev):
+    """Device metadata outside its documented range is not checked (as on the
+    page); the kernel guards against faults instead: a state slot at or past
+    `slots` is skipped, accepted counts are clamped to [0, T], and a track
+    slot at or past `slots` leaves the tracked step unwritten.  The result
+    must equal the oracle's on metadata sanitised that way (the oracle itself
+    rejects such values)."""
+    import copy
+    spec = ri.with_(ri.GDN_CONFIGS["gdn_small"], B=8, slots=24, null_frac=0.0, zero_frac=0.0)
+    bad = ri.make_gdn_problem(spec, 74)
+    T, S, null = spec.T, spec.slots, spec.null_block_id
+    bad.accept_lens = bad.accept_lens.copy()
+    bad.state_indices = bad.state_indices.copy()
+    bad.track_state_indices = bad.track_state_indices.copy()
+    bad.track_steps = bad.track_steps.copy()
+    bad.accept_lens[0] = T + 5                # clamped to T
+    bad.accept_lens[1] = -3                   # clamped to 0: nothing committed
+    bad.state_indices[2] = S + 4              # out of range: skipped
+    bad.track_state_indices[3] = S + 7        # out of range: tracked step not written
+    bad.track_steps[3] = 0
+    sane = copy.copy(bad)
+    sane.accept_lens = np.clip(bad.accept_lens, 0, T).astype(bad.accept_lens.dtype)
+    sane.state_indices = np.where(bad.state_indices >= S, null, bad.state_indices).astype(bad.state_indices.dtype)
+    sane.track_state_indices = np.where(bad.track_state_indices >= S, null,
+                                        bad.track_state_indices).astype(bad.track_state_indices.dtype)
+    say("out-of-range metadata")
+    check(sane, run(bad, dev), "out-of-range metadata")
+
+
 def test_nothing_to_commit(dev):
     spec = ri.with_(ri.GDN_CONFIGS["gdn_small"], accept=[0] * 6)
     prob = ri.make_gdn_problem(spec, 73)

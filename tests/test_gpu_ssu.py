@@ -126,6 +126,33 @@ def test_variants(dev, kw):
     check(prob, run(prob, dev), str(kw))
 
 
+def test_out_of_range_metadata_guards(dev):
+    """Device metadata outside its documented range is not checked; the
+    kernel guards against faults instead: a slot outside [0, num_slots) is
+    skipped (its outputs stay unwritten), ring_start is taken modulo R and
+    num_buffered is clamped to [0, min(16, R) - T].  The result must equal
+    the oracle's on metadata sanitised that way (the oracle itself rejects
+    such values)."""
+    import copy
+    spec = ri.with_(ri.SSU_CONFIGS["ssu_small"], B=6, pad_frac=0.0)
+    bad = ri.make_ssu_problem(spec, 86)
+    R, T, pad = spec.R, spec.T, spec.pad_slot_id
+    n_slots = bad.pools.meta.slots
+    for name in ("slots", "ring_start", "num_buffered"):
+        setattr(bad, name, getattr(bad, name).copy())
+    bad.num_buffered[0] = 30                  # clamped to min(16, R) - T
+    bad.num_buffered[1] = -2                  # clamped to 0
+    bad.ring_start[2] = -5                    # taken modulo R
+    bad.ring_start[3] = 2 * R + 3
+    bad.slots[4] = n_slots + 2                # out of range: skipped
+    sane = copy.copy(bad)
+    sane.num_buffered = np.clip(bad.num_buffered, 0, min(16, R) - T).astype(np.int32)
+    sane.ring_start = np.mod(bad.ring_start, R).astype(np.int32)
+    sane.slots = np.where((bad.slots < 0) | (bad.slots >= n_slots), pad, bad.slots).astype(np.int32)
+    say("out-of-range metadata")
+    check(sane, run(bad, dev), "out-of-range metadata")
+
+
 def test_grid_invariance(dev):
     """Each (request, head) item's arithmetic is independent of the launch
     shape: outputs and rings are identical bytes for any grid."""
