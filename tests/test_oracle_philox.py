@@ -80,3 +80,45 @@ def test_philox_output_is_uniform(orc):
     words = np.concatenate([orc.philox4x32([i, 0, 0, 0], [1234, 0], 10) for i in range(2000)]).astype(np.float64)
     u = words / 2.0**32
     assert abs(u.mean() - 0.5) < 4 * np.sqrt(1 / 12 / u.size)
+
+
+@pytest.mark.parametrize("state", ["bf16", "i8"])
+def test_sr_word_of_each_element_is_the_mapped_rocrand_word(orc, rocrand_ref, state):
+    """Which random word each element's stochastic rounding uses (the
+    library's reading of the pages' "Philox seed derivation"): counter
+    ((r * dstate + c) / 4, head, request, layer), key (low, high) 32-bit words
+    of the seed, output word c mod 4.  Every element sits exactly halfway
+    between two codes, so it rounds up iff its word is below 2^31; the words
+    come from rocRAND's generator with that mapping written out here, not
+    from the oracle.  A wrong counter word, a swapped key or counter pair, or
+    another output word each flip about half the elements."""
+    import rssm_inputs as ri
+    seed = 0x0123456789ABCDEF
+    ds = 16
+    spec = ri.with_(ri.CONFIGS["tiny_f32"], dstate=ds, state_dtype=state, philox_rounds=10, rand_seed=seed)
+    if state == "bf16":
+        row = np.full(ds, 1.0 + 2.0 ** -8, np.float32)     # halfway between bf16 1 and 1 + 2^-7
+        lo, hi = 0x3F80, 0x3F81
+    else:
+        row = np.full(ds, 10.5, np.float32)                # row max 127: t = v, halfway between 10 and 11
+        row[0] = 127.0
+        lo, hi = 10, 11
+    coords = [(l, b, h, r) for l in (0, 5) for b in (0, 3, 200) for h in (0, 7) for r in (0, 1, 13)]
+    rows, want = [], []
+    for (l, b, h, r) in coords:
+        for c in range(ds):
+            rows.append([(r * ds + c) // 4, h, b, l, seed & 0xFFFFFFFF, seed >> 32])
+    words = rocrand_ref(np.array(rows, np.uint64))
+    n_up = 0
+    for i, (l, b, h, r) in enumerate(coords):
+        codes, _ = orc.encode_row(spec, row, l, b, h, r)
+        codes = np.asarray(codes).view(np.uint16 if state == "bf16" else np.int8).astype(np.int64)
+        for c in range(ds):
+            if state == "i8" and c == 0:
+                continue                                   # exact 127
+            u = int(words[i * ds + c][c % 4])
+            expect = hi if u < 2 ** 31 else lo
+            assert codes[c] == expect, f"layer {l} request {b} head {h} row {r} col {c}: code {codes[c]}, word {u:#x}"
+            n_up += expect == hi
+    total = len(coords) * (ds - (1 if state == "i8" else 0))
+    assert 0.35 * total < n_up < 0.65 * total              # both directions occur
