@@ -69,6 +69,14 @@ def test_nearest_even_matches_torch(orc, dtype):
     got = np.array([orc.round_value(dtype, v) for v in vals], np.uint32)
     bad = got != ref
     assert not bad.any(), list(zip(vals[bad][:5], got[bad][:5], ref[bad][:5]))
+    # NaN of either sign: torch's fp16 and e4m3 casts keep the sign, as the
+    # oracle does; its bf16 cast returns 0xFFFF for both, so there only the
+    # NaN-ness is compared (the sign of a converted NaN is unspecified)
+    nans = np.array([np.float32("nan"), -np.float32("nan")], np.float32)
+    got_nan = np.array([orc.round_value(dtype, v) for v in nans], np.uint32)
+    assert np.isnan(orc.decode(dtype, got_nan.astype(raw.dtype))).all()
+    if dtype != "bf16":
+        np.testing.assert_array_equal(got_nan, torch_codes(dtype, nans))
 
 
 def test_bf16_f16_overflow_to_infinity(orc):
@@ -181,3 +189,30 @@ def test_row_quantization_e3_e4(orc):
     zero = np.zeros(16, np.float32)
     codes, scale = orc.encode_row(spec, zero, 0, 0, 0, 0, state_dtype="i8", philox_rounds=0)
     assert scale == 0.0 and not codes.any()
+
+
+def test_nan_element_in_one_byte_row(orc):
+    """A NaN element takes no part in a one-byte row's quantization: the row
+    scale and every other code equal those of the same row with that element
+    set to 0, with nearest-even and with stochastic rounding (each element's
+    random word depends on its own coordinates only).  The NaN element itself
+    takes the codes the design reads for it: 0 for int8, S.1111.111 (its own
+    sign) for e4m3."""
+    import rssm_inputs as ri
+    spec = ri.CONFIGS["tiny_f32"]
+    rng = np.random.default_rng(21)
+    for dt in ("i8", "f8e4m3"):
+        for rounds in (0, 10):
+            for sign in (1.0, -1.0):
+                row = (rng.standard_normal(16) * 3).astype(np.float32)
+                ref_row = row.copy()
+                ref_row[5] = 0.0
+                row[5] = np.copysign(np.float32("nan"), np.float32(sign))   # (a product would keep +NaN)
+                codes, scale = orc.encode_row(spec, row, 1, 2, 3, 4, state_dtype=dt, philox_rounds=rounds, seed=29)
+                ref, ref_scale = orc.encode_row(spec, ref_row, 1, 2, 3, 4, state_dtype=dt, philox_rounds=rounds,
+                                                seed=29)
+                assert scale == ref_scale and scale > 0
+                keep = np.arange(16) != 5
+                np.testing.assert_array_equal(np.asarray(codes)[keep], np.asarray(ref)[keep])
+                nan_code = int(np.asarray(codes).view(np.uint8)[5])
+                assert nan_code == (0 if dt == "i8" else (0xFF if sign < 0 else 0x7F))
