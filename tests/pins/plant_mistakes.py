@@ -54,6 +54,16 @@ M = [
  ("checkpoints: no pre-call snapshot", "ins = _Inputs(state=_ptr_array(state_in), state_stride=_i64(meta.state_stride),\n                      scale=_ptr_array(scale_in) if scale_in else None,", "ins = _Inputs(state=_ptr_array(state_out), state_stride=_i64(meta.state_stride),\n                      scale=_ptr_array(scale_out) if scale_out else None,", "__init__.py"),
  ("checkpoints: first prefix table for all", "pf = np.ascontiguousarray(pref, np.int32)", "pf = np.ascontiguousarray(prefix_list[0], np.int32)", "__init__.py"),
  ("checkpoints: first destination table for all", "dst_arr = np.ascontiguousarray(dst, np.int32)", "dst_arr = np.ascontiguousarray(dst_list[0], np.int32)", "__init__.py"),
+ ("gdn: decay after the update",
+  ("    for (int i = 0; i < dv * dk; ++i) S[i] *= alpha;\n", "    if (t == track_step) {"),
+  ("", "    for (int i = 0; i < dv * dk; ++i) S[i] *= alpha;\n    if (t == track_step) {"), "gdn_oracle.c"),
+ ("gdn: wrong key-head map", "(((int64_t)l * p->slots + s) * H + hv / group);", "(((int64_t)l * p->slots + s) * H + hv % H);", "gdn_oracle.c"),
+ ("gdn: keys not normalised", "if (p->use_l2norm) {", "if (0) {", "gdn_oracle.c"),
+ ("gdn: tracked step off by one", "if (t == track_step) {", "if (t == track_step + 1) {", "gdn_oracle.c"),
+ ("gdn: update sign", "const double u = beta * (v - Sk[i]);", "const double u = beta * (Sk[i] - v);", "gdn_oracle.c"),
+ ("gdn: epsilon outside the root", "const double nrm = sqrt(ss + 1e-6);", "const double nrm = sqrt(ss) + 1e-6;", "gdn_oracle.c"),
+ ("gdn: transposed product S k", "acc += S[(size_t)i * dk + j] * k[j];", "acc += S[(size_t)j * dk + i] * k[j];", "gdn_oracle.c"),
+ ("gdn: beta inside the bracket", "const double u = beta * (v - Sk[i]);", "const double u = beta * v - Sk[i];", "gdn_oracle.c"),
  ("ssu: C of the wrong group", "const int64_t cbase = (((int64_t)b * T + t) * G + g) * ds;", "const int64_t cbase = (((int64_t)b * T + t) * G + (G - 1 - g)) * ds;", "ssu_oracle.c"),
 ]
 def run(name, old, new, fname="rssm_oracle.c"):
@@ -63,8 +73,11 @@ def run(name, old, new, fname="rssm_oracle.c"):
     if old is not None:
         p = os.path.join(d, "oracle", fname)
         s = open(p).read()
-        assert s.count(old) == 1, (name, s.count(old))
-        open(p, "w").write(s.replace(old, new))
+        pairs = zip(old, new) if isinstance(old, tuple) else [(old, new)]
+        for o, n in pairs:
+            assert s.count(o) == 1, (name, s.count(o))
+            s = s.replace(o, n)
+        open(p, "w").write(s)
     subprocess.check_call([sys.executable, "-c", "import oracle; oracle.build()"], cwd=d)
     tests = sorted(f"tests/{f}" for f in os.listdir(os.path.join(d, "tests")) if f.startswith("test_oracle_"))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", *tests], cwd=d,
