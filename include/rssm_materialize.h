@@ -19,9 +19,9 @@
  * allocates nothing, keeps no reference after it returns, and reads no
  * device memory on the host (it never synchronises).  The caller keeps
  * every buffer alive until the enqueued work has completed on the stream.
- * (rssm_pool.h, a placement helper outside this boundary, hands out
- * physically contiguous device memory for the pools; the operation works on
- * any device memory.)
+ * (rssm_pool.h, a placement helper in a library of its own, librssm_pool,
+ * outside this boundary, hands out physically contiguous device memory for
+ * the pools; the operation works on any device memory.)
  */
 #ifndef RSSM_MATERIALIZE_H
 #define RSSM_MATERIALIZE_H

@@ -1,9 +1,10 @@
 /*
- * rssm_pool.h -- physically contiguous device memory for the state pools of
- * librssm_materialize (MI355X, gfx950).
+ * rssm_pool.h -- C ABI of librssm_pool: physically contiguous device memory
+ * for the state pools of librssm_materialize (MI355X, gfx950).
  *
  * Not an operation of the pages and not part of the operation's boundary
- * (rssm_materialize.h): a placement helper for the pools that the
+ * (rssm_materialize.h): a placement helper, built as a library of its own so
+ * that librssm_materialize exports nothing that allocates, for the pools that the
  * materialize, commit and decode kernels stream (tens of GiB per layer set),
  * used by the benchmark and the tests to place their pools.  The operation
  * entry points accept any device memory and allocate nothing themselves; only

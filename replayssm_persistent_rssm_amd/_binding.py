@@ -14,12 +14,15 @@ from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librssm_materialize.so")
+# the contiguous-pool placement helper (rssm_pool.h): a library of its own,
+# outside the operation's boundary
+POOL_LIB_PATH = os.path.join(_PKG, "librssm_pool.so")
 
 RSSM_F32, RSSM_BF16, RSSM_F16, RSSM_I8, RSSM_F8E4M3 = 0, 1, 2, 3, 4
 RSSM_OK, RSSM_ERR_INVALID_ARGUMENT, RSSM_ERR_UNSUPPORTED, RSSM_ERR_HIP = 0, 1, 2, 3
 EXPORTS = ("rssm_materialize", "rssm_materialize_checkpoints", "rssm_last_error", "rssm_materialize_launch_config",
-           "rssm_debug_encode_rows", "rssm_debug_row_scales", "rssm_gdn_commit", "rssm_ssu_decode", "rssm_pool_alloc", "rssm_pool_free",
-           "rssm_torch_pool_alloc", "rssm_torch_pool_free")
+           "rssm_debug_encode_rows", "rssm_debug_row_scales", "rssm_gdn_commit", "rssm_ssu_decode")
+POOL_EXPORTS = ("rssm_pool_alloc", "rssm_pool_free", "rssm_torch_pool_alloc", "rssm_torch_pool_free")
 RSSM_MAX_CHECKPOINTS = 4
 RSSM_SSU_MAX_TOKENS = 8
 RSSM_SSU_MAX_REPLAY = 16
@@ -92,10 +95,6 @@ def _load():
     lib.rssm_gdn_commit.restype = ctypes.c_int
     lib.rssm_ssu_decode.argtypes = [ctypes.POINTER(RssmSsuDesc), ctypes.POINTER(RssmSsuTables), ctypes.c_void_p]
     lib.rssm_ssu_decode.restype = ctypes.c_int
-    lib.rssm_pool_alloc.argtypes = [ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int32)]
-    lib.rssm_pool_alloc.restype = ctypes.c_int
-    lib.rssm_pool_free.argtypes = [ctypes.c_void_p]
-    lib.rssm_pool_free.restype = ctypes.c_int
     lib.rssm_last_error.argtypes = []
     lib.rssm_last_error.restype = ctypes.c_char_p
     lib.rssm_materialize_launch_config.argtypes = [ctypes.POINTER(RssmDesc), ctypes.POINTER(ctypes.c_int32),
@@ -112,10 +111,27 @@ def _load():
 
 
 _lib = _load()
+_pool = None
 
 
 def lib():
     return _lib
+
+
+def pool_lib():
+    """The placement helper's library (loaded on first use)."""
+    global _pool
+    if _pool is None:
+        if not os.path.exists(POOL_LIB_PATH):
+            raise ImportError(f"{POOL_LIB_PATH} is not built. Build it with "
+                              "`python -m replayssm_persistent_rssm_amd.build` (or __graft_entry__.build()).")
+        pl = ctypes.CDLL(POOL_LIB_PATH)
+        pl.rssm_pool_alloc.argtypes = [ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int32)]
+        pl.rssm_pool_alloc.restype = ctypes.c_int
+        pl.rssm_pool_free.argtypes = [ctypes.c_void_p]
+        pl.rssm_pool_free.restype = ctypes.c_int
+        _pool = pl
+    return _pool
 
 
 def rssm_last_error() -> str:
@@ -459,24 +475,27 @@ def rssm_pool_alloc(nbytes: int):
     """(address, contiguous) of `nbytes` of device memory on the current
     device, physically contiguous when possible (rssm_pool.h)."""
     out, contig = ctypes.c_void_p(), ctypes.c_int32()
-    st = _lib.rssm_pool_alloc(ctypes.c_uint64(int(nbytes)), ctypes.byref(out), ctypes.byref(contig))
+    st = pool_lib().rssm_pool_alloc(ctypes.c_uint64(int(nbytes)), ctypes.byref(out), ctypes.byref(contig))
     if st != RSSM_OK:
         raise RssmError(st, "rssm_pool_alloc failed" if st == RSSM_ERR_HIP else "invalid size")
     return out.value, bool(contig.value)
 
 
 def rssm_pool_free(addr) -> None:
-    _check(_lib.rssm_pool_free(ctypes.c_void_p(addr)))
+    st = pool_lib().rssm_pool_free(ctypes.c_void_p(addr))
+    if st != RSSM_OK:
+        raise RssmError(st, "rssm_pool_free failed")
 
 
 def use_contiguous_allocator() -> None:
     """Route every torch device allocation of this process through the
-    library's contiguous pool allocator (rssm_torch_pool_alloc /
+    contiguous pool allocator of librssm_pool (rssm_torch_pool_alloc /
     rssm_torch_pool_free; no caching: each free waits for the device).  Must
     run before the process allocates any device memory.  On MI355X a large
     pool from a plain allocation can stream markedly slower (rssm_pool.h)."""
     import torch
-    alloc = torch.cuda.memory.CUDAPluggableAllocator(LIB_PATH, "rssm_torch_pool_alloc", "rssm_torch_pool_free")
+    pool_lib()   # fails loudly if the helper library is not built
+    alloc = torch.cuda.memory.CUDAPluggableAllocator(POOL_LIB_PATH, "rssm_torch_pool_alloc", "rssm_torch_pool_free")
     torch.cuda.memory.change_current_allocator(alloc)
 
 

@@ -1,4 +1,6 @@
-"""Build librssm_materialize.so for gfx950 with hipcc (in-tree, no JIT).
+"""Build librssm_materialize.so (the operation) and librssm_pool.so (the
+contiguous-pool placement helper, a separate library so that the operation's
+library exports nothing that allocates) for gfx950 with hipcc, in-tree, no JIT.
 
 Each state dtype's kernel instances live in their own translation unit and
 compile in parallel; the host launcher is one more.  Flags: -O3, C++17,
@@ -18,10 +20,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "librssm_materialize.so")
+POOL_LIB_PATH = os.path.join(PKG, "librssm_pool.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["rssm_inst_f32.hip", "rssm_inst_bf16.hip", "rssm_inst_f16.hip", "rssm_inst_i8.hip",
-           "rssm_inst_f8.hip", "rssm_inst_gdn.hip", "rssm_inst_ssu.hip", "rssm_pool.hip", "rssm_materialize.hip"]
+           "rssm_inst_f8.hip", "rssm_inst_gdn.hip", "rssm_inst_ssu.hip", "rssm_materialize.hip"]
+POOL_SOURCES = ["rssm_pool.hip"]
 ARCH = os.environ.get("RSSM_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -45,18 +49,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"link of {os.path.basename(path)} failed:\n" + res.stderr)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile and link both libraries; returns the operation library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + POOL_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], POOL_LIB_PATH, verbose)
     return LIB_PATH
 
 

@@ -19,19 +19,33 @@ def rp():
     return rp
 
 
-def declared_functions():
+POOL_HEADER = os.path.join(ROOT, "include", "rssm_pool.h")
+
+
+def declared_functions(headers):
     names = set()
-    for h in HEADERS:
+    for h in headers:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
         names |= set(re.findall(r"\b(rssm_[a-z_]+)\s*\(", text))
     return sorted(names)
 
 
 def test_library_exports_every_declared_entry_point(rp):
-    names = declared_functions()
+    """librssm_materialize exports every entry point its headers declare."""
+    names = declared_functions([h for h in HEADERS if h != POOL_HEADER])
     assert names == sorted(rp.EXPORTS)
     for n in names:
         assert hasattr(rp.lib(), n), n
+
+
+def test_pool_helper_is_a_separate_library(rp):
+    """rssm_pool.h's allocating helpers live in librssm_pool alone: the
+    operation's library exports none of them."""
+    names = declared_functions([POOL_HEADER])
+    assert names == sorted(rp.POOL_EXPORTS)
+    for n in names:
+        assert hasattr(rp.pool_lib(), n), n
+        assert not hasattr(rp.lib(), n), f"{n} is exported by the operation's library"
 
 
 def _desc(rp, **kw):
@@ -303,7 +317,7 @@ def test_ssu_byte_count():
 def test_pool_alloc_validation(rp):
     """Host validation of the pool allocator, before any HIP call."""
     out = ctypes.c_void_p(123)
-    assert rp.lib().rssm_pool_alloc(ctypes.c_uint64(1 << 20), None, None) == 1
-    assert rp.lib().rssm_pool_alloc(ctypes.c_uint64(0), ctypes.byref(out), None) == 1
+    assert rp.pool_lib().rssm_pool_alloc(ctypes.c_uint64(1 << 20), None, None) == 1
+    assert rp.pool_lib().rssm_pool_alloc(ctypes.c_uint64(0), ctypes.byref(out), None) == 1
     assert out.value is None
-    assert rp.lib().rssm_pool_free(None) == 0
+    assert rp.pool_lib().rssm_pool_free(None) == 0
