@@ -44,7 +44,7 @@ M = [
  ("NaN sign dropped (f16)", "case ORC_F16: return (negative ? 0x8000u : 0u) | 0x7E00u;", "case ORC_F16: return 0x7E00u;"),
  ("int8 NaN to 127", "default: return 0u; /* int8: NaN encodes as 0 */", "default: return 127u;"),
  ("Philox multiplier swapped", "uint64_t p0 = (uint64_t)M0 * (uint64_t)c0;\n    uint64_t p1 = (uint64_t)M1 * (uint64_t)c2;", "uint64_t p0 = (uint64_t)M1 * (uint64_t)c0;\n    uint64_t p1 = (uint64_t)M0 * (uint64_t)c2;"),
- ("Philox key bump before round 0", "if (i > 0) { k0 += W0; k1 += W1; }", "{ k0 += W0; k1 += W1; }"),
+ ("Philox key bump before the first Philox round", "if (i > 0) { k0 += W0; k1 += W1; }", "{ k0 += W0; k1 += W1; }"),
  ("ssu: append ignores pending count", "const int32_t e = (r0 + n + t) % R;", "const int32_t e = (r0 + t) % R;", "ssu_oracle.c"),
  ("ssu: pending entry off by one", "const int32_t e = (r0 + j) % R;", "const int32_t e = (r0 + j + 1) % R;", "ssu_oracle.c"),
  ("ssu: no dt bias on replayed new tokens", "          if (in->dt_bias) dt += (double)in->dt_bias[h];\n          if (p->dt_softplus) dt = softplus(dt);\n          xb = in->x_new;", "          if (p->dt_softplus) dt = softplus(dt);\n          xb = in->x_new;", "ssu_oracle.c"),
