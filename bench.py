@@ -101,6 +101,25 @@ def traffic_from_profile(workload: str = "large_bf16"):
         return None
 
 
+VALU_FILE = "valu_counters_by_workload.txt"
+VALU_PEAK_PER_S = 1024 * 2.4e9 / 4   # wave64 VALU instructions per second: 1024 SIMDs, 4 cycles each
+
+
+def valu_instructions(workload: str):
+    """SQ_INSTS_VALU per call of a materialize workload from the committed
+    vector-ALU table, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", VALU_FILE)
+    if workload not in ("large_bf16", "large_i8", "large_f8sr") or not os.path.exists(path):
+        return None
+    current = None
+    for line in open(path):
+        if line.startswith("kernel_source_hash (materialize):"):
+            current = line.split(":", 1)[1].strip() == kernel_hash(COUNTER_SOURCES["large_bf16"])
+        elif current and line.startswith(workload + " |"):
+            return float(line.split("|")[3])
+    return None
+
+
 def traffic_ratio(workload: str):
     """Counter traffic over algorithmic bytes from the committed summary (None
     if it is missing or was taken on other kernel code)."""
@@ -792,6 +811,10 @@ def other_workload(name, dev, stream, steps):
            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "us_per_request": round(ms * 1e3 / n, 3),
            "traffic_over_algorithmic": traffic_ratio(name)}
+    ins = valu_instructions(name)
+    if ins is not None:
+        # the vector-ALU roofline: committed instruction count over this run's time
+        out["valu_issue_frac"] = round(ins / VALU_PEAK_PER_S / (ms * 1e-3), 4)
     out.update(empty_launch_costs(dp, tabs, spec, stream))
     out["grid"] = rp.rssm_materialize_launch_config(
         num_layers=spec.L, batch=spec.B, num_heads=spec.H, heads_per_group=spec.hpg, dim=spec.dim,

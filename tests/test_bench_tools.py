@@ -107,3 +107,21 @@ def test_valu_summary_row(tmp_path):
     assert float(cells[6]) == pytest.approx(2.4e9 * 4 / 1024 / 2.4e9 * 1e3, rel=1e-3)
     assert int(cells[7]) == 1600000000
     assert float(cells[8]) == pytest.approx(2.4e9 * 64 / 1.6e9, abs=0.01)
+
+
+def test_valu_instructions_follow_the_hash_rule(tmp_path, monkeypatch):
+    """The vector-ALU figure of a materialize workload comes from the committed
+    table only while its kernel_source_hash line matches the current source."""
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "k.h").write_text("__global__ void k() {}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setitem(bench.COUNTER_SOURCES, "large_bf16", ["k.h"])
+    table = tmp_path / "profiles" / bench.VALU_FILE
+    rows = ("# header\n" + bench.VALU_HEADER + "\n"
+            "large_i8 | materialize_kernel | 4096 | 6.1679e+08 | 6.2e+08 | 3.5e+07 | 1.004 | 6442450944 | 6.13\n")
+    table.write_text(f"kernel_source_hash (materialize): {bench.kernel_hash(['k.h'])}\n" + rows)
+    assert bench.valu_instructions("large_i8") == pytest.approx(6.1679e8)
+    assert bench.valu_instructions("large_f8sr") is None          # no row
+    assert bench.valu_instructions("gdn_large") is None           # not a materialize workload
+    table.write_text("kernel_source_hash (materialize): 0000000000000000\n" + rows)
+    assert bench.valu_instructions("large_i8") is None
