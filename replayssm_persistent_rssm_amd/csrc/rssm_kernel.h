@@ -22,12 +22,17 @@
 //    and, within a head group, the B rows, which stay in registers.
 //  * Decay weights come from a wavefront-level suffix-product scan over the k
 //    per-token decays a_j = exp(dt_j A_h) held one per lane.
-//  * w_j * x_j is staged per wavefront in LDS ([row][token], fp32); each lane
-//    owns 8 columns, keeps B_j for those columns in registers (16-token
-//    windows: tokens 0..3 in registers, 4..15 in the wavefront's LDS), and
-//    streams its rows of the tile through registers with 16-byte loads (8-byte
-//    for one-byte state), folding k multiply-adds per element.  No MFMA: the
-//    path moves ~4 bytes per 2k+1 flops and is bound by HBM.
+//  * Vector-ALU fold (fp32, bf16 and fp16 state; every multi-checkpoint
+//    instance): w_j * x_j is staged per wavefront in LDS ([row][token],
+//    fp32); each lane owns 8 columns, keeps B_j for those columns in
+//    registers (16-token windows: tokens 0..3 in registers, 4..15 in the
+//    wavefront's LDS), and streams its rows of the tile through registers
+//    with 16-byte loads, folding k multiply-adds per element.  These paths
+//    move ~4 bytes per 2k+1 flops and are bound by HBM, so no matrix cores.
+//  * Matrix-core fold (one-byte state, one checkpoint; mfma_fold_heads):
+//    there the per-element decode, row scale and encode make the vector ALU
+//    the limit, so the fold itself moves to fp32 16x16x4 MFMA on 16-row
+//    blocks and the vector ALU keeps only the decode and encode.
 //  * No workgroup barriers: the four waves of a workgroup are independent.
 #pragma once
 
