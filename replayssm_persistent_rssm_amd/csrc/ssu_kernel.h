@@ -371,7 +371,16 @@ __global__ void __launch_bounds__(kBlock, (kSsuWavesPerSimd<ST, IT, TMAX>)) ssu_
   const int64_t tw = static_cast<int64_t>(gridDim.x) * kWaves;
   constexpr int64_t kC = 16;
   const int64_t csz = min(kC, (items + tw - 1) / tw);
-  int64_t chunk = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  // Workgroups go to the eight XCDs (each with its own L2) in turn.  Within
+  // every run of 64 workgroups, the eight that one XCD receives take eight
+  // consecutive item ranges, so the heads of one B group (whose B and C rows
+  // every wavefront of the group reads) share an L2, while the run as a whole
+  // still covers one contiguous stretch of tiles.  (Measured on MI355X,
+  // ssu_large: 212.9 against 214.2 us; one contiguous eighth of the grid per
+  // XCD instead ran 225 us, since the tiles in flight then lie far apart.)
+  int64_t bid = blockIdx.x;
+  if (bid < static_cast<int64_t>(gridDim.x / 64) * 64) bid = (bid / 64) * 64 + (bid % 8) * 8 + (bid % 64) / 8;
+  int64_t chunk = bid * kWaves + wave;
   int64_t nxt = chunk * csz;                         // next item not yet taken (-1: none)
   int64_t cend = min(items, nxt + csz);
   if (nxt >= items) nxt = -1;
