@@ -9,7 +9,7 @@
  * DIR/problem.txt holds whitespace-separated integers:
  *   num_layers batch num_heads heads_per_group dim dstate max_window
  *   ring_buffer_len pad_slot_id philox_rounds state_dtype input_dtype
- *   max_workgroups has_scale has_seed
+ *   max_workgroups has_scale has_seed num_checkpoints
  * followed, for each layer, by its slot strides in elements:
  *   state scale x B dt
  * DIR also holds one raw little-endian blob per buffer (the layouts of
@@ -17,13 +17,15 @@
  *   state_<l>.bin x_<l>.bin B_<l>.bin dt_<l>.bin A_<l>.bin [scale_<l>.bin]
  *   src.bin dst.bin ([L][B] int32)  ring_start.bin prefix.bin active.bin
  *   ([B] int32)  [seed.bin (one int64)]
+ * num_checkpoints 0 makes one rssm_materialize call; C >= 1 makes one
+ * rssm_materialize_checkpoints call with C tables: dst.bin then holds
+ * [C][L][B] and prefix.bin [C][B] int32.
  *
  * The program reads every blob, checks on the host (before any HIP call) that
  * every slot the call will touch lies inside its pool, uploads each blob to a
  * device allocation of its own, builds the pointer and stride tables, prints
  * the launch the library would make, checks that an invalid descriptor is
- * refused with a message, makes one rssm_materialize call on a stream it
- * creates, waits for it, checks that the rings, A and the metadata came back
+ * refused with a message, makes the call on a stream it creates, waits for it, checks that the rings, A and the metadata came back
  * unchanged, and writes state_<l>.out (and scale_<l>.out) with the pools as
  * the call left them.
  *
@@ -158,13 +160,15 @@ int main(int argc, char **argv) {
   if (!pf) die(1, "cannot open", path);
   rssm_materialize_desc desc;
   memset(&desc, 0, sizeof desc);
-  int has_scale = 0, has_seed = 0;
+  int has_scale = 0, has_seed = 0, ncp = 0;
   desc.a_dtype = RSSM_F32;
-  if (fscanf(pf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d", &desc.num_layers, &desc.batch,
+  if (fscanf(pf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d", &desc.num_layers, &desc.batch,
              &desc.num_heads, &desc.heads_per_group, &desc.dim, &desc.dstate, &desc.max_window,
              &desc.ring_buffer_len, &desc.pad_slot_id, &desc.philox_rounds, &desc.state_dtype,
-             &desc.input_dtype, &desc.max_workgroups, &has_scale, &has_seed) != 15)
+             &desc.input_dtype, &desc.max_workgroups, &has_scale, &has_seed, &ncp) != 16)
     die(1, "malformed header in", path);
+  if (ncp < 0 || ncp > RSSM_MAX_CHECKPOINTS) die(1, "num_checkpoints out of range in", path);
+  const int C = ncp > 0 ? ncp : 1;  /* destination and prefix tables */
   const int L = desc.num_layers, B = desc.batch;
   if (L < 1 || L > MAX_LAYERS || B < 1 || desc.num_heads < 1 || desc.heads_per_group < 1 ||
       desc.num_heads % desc.heads_per_group)
@@ -193,7 +197,7 @@ int main(int argc, char **argv) {
   load("active", -1, 1, &active);
   if (has_seed) load("seed", -1, 1, &seed); else memset(&seed, 0, sizeof seed);
   const size_t LB = (size_t)L * B * sizeof(int32_t), B4 = (size_t)B * sizeof(int32_t);
-  if (src.bytes != LB || dst.bytes != LB || ring_start.bytes != B4 || prefix.bytes != B4 ||
+  if (src.bytes != LB || dst.bytes != C * LB || ring_start.bytes != B4 || prefix.bytes != C * B4 ||
       active.bytes != B4 || (has_seed && seed.bytes != sizeof(int64_t)))
     die(1, "a metadata blob has the wrong size", NULL);
 
@@ -206,19 +210,28 @@ int main(int argc, char **argv) {
   const int32_t *rs = (const int32_t *)ring_start.host;
   for (int i = 0; i < B && act[i] >= 0 && act[i] < B; ++i) {
     const int b = act[i];
-    if (pre[b] < 0 || pre[b] > desc.max_window || rs[b] < 0 || rs[b] >= desc.ring_buffer_len)
-      die(1, "prefix length or ring start outside the contract", NULL);
+    if (rs[b] < 0 || rs[b] >= desc.ring_buffer_len) die(1, "ring start outside the contract", NULL);
+    for (int c = 0; c < C; ++c)
+      if (pre[(size_t)c * B + b] < 0 || pre[(size_t)c * B + b] > desc.max_window)
+        die(1, "prefix length outside the contract", NULL);
     for (int l = 0; l < L; ++l) {
-      const int32_t s = srcs[(size_t)l * B + b], d = dsts[(size_t)l * B + b];
-      if (s == desc.pad_slot_id || d == desc.pad_slot_id) continue;
+      const int32_t s = srcs[(size_t)l * B + b];
+      if (s == desc.pad_slot_id) continue;
       const int64_t ns = pool_slots(&state[l], strides[0][l], sb);
       const int64_t nr = pool_slots(&x[l], strides[2][l], ib);
       if (ns < 0 || nr < 0 || pool_slots(&Bm[l], strides[3][l], ib) != nr ||
           pool_slots(&dt[l], strides[4][l], 4) != nr ||
           (has_scale && pool_slots(&scale[l], strides[1][l], 4) != ns))
         die(1, "a pool is not a whole number of slots", NULL);
-      if (s < 0 || d < 0 || s >= ns || d >= ns || s >= nr) die(1, "a slot lies outside its pool", NULL);
       if (A[l].bytes != (size_t)desc.num_heads * 4) die(1, "A has the wrong size", NULL);
+      int live = 0;
+      for (int c = 0; c < C; ++c) {
+        const int32_t d = dsts[((size_t)c * L + l) * B + b];
+        if (d == desc.pad_slot_id) continue;
+        if (d < 0 || d >= ns) die(1, "a slot lies outside its pool", NULL);
+        live = 1;
+      }
+      if (live && (s < 0 || s >= ns || s >= nr)) die(1, "a slot lies outside its pool", NULL);
     }
   }
 
@@ -283,8 +296,9 @@ int main(int argc, char **argv) {
 
   hipStream_t stream;
   HIP_OK(hipStreamCreate(&stream));
-  st = rssm_materialize(&desc, &tab, (void *)stream);
-  if (st != RSSM_OK) die(2, "rssm_materialize", rssm_last_error());
+  st = ncp > 0 ? rssm_materialize_checkpoints(&desc, &tab, ncp, (void *)stream)
+              : rssm_materialize(&desc, &tab, (void *)stream);
+  if (st != RSSM_OK) die(2, ncp > 0 ? "rssm_materialize_checkpoints" : "rssm_materialize", rssm_last_error());
   HIP_OK(hipStreamSynchronize(stream));
   HIP_OK(hipStreamDestroy(stream));
   printf("materialize ok\n");
