@@ -165,6 +165,23 @@ def test_grid_invariance(dev):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), g
 
 
+def test_xcd_block_order_runs_and_tail(dev):
+    """The kernel renumbers workgroups within each full run of 64 so that one
+    XCD's eight take consecutive items; the tail keeps launch order.  368
+    items give a default grid of 92 workgroups (one run and a tail of 28):
+    against the oracle, and byte-identical at grids of 64 (one run), 128 (two),
+    130 (two and a tail) and 1."""
+    spec = ri.with_(ri.SSU_CONFIGS["ssu_small"], B=23, H=16, hpg=8, pad_frac=0.1)
+    prob = ri.make_ssu_problem(spec, 87)
+    say("block order: B=23 H=16, default grid 92")
+    ref = run(prob, dev)
+    check(prob, ref, "block order, default grid")
+    for g in (64, 128, 130, 1):
+        got = run(prob, dev, max_workgroups=g)
+        for a, b in zip(got, ref):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), g
+
+
 def test_empty_batch(dev):
     import torch
     import replayssm_persistent_rssm_amd as rp
