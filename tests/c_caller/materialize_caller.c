@@ -4,7 +4,7 @@
  * a test can show the boundary stands on its own.  Test infrastructure: it
  * computes nothing of the method itself.
  *
- * Usage: materialize_caller DIR
+ * Usage: materialize_caller DIR [EMPTY_CALLS]
  *
  * DIR/problem.txt holds whitespace-separated integers:
  *   num_layers batch num_heads heads_per_group dim dstate max_window
@@ -28,6 +28,11 @@
  * refused with a message, makes the call on a stream it creates, waits for it, checks that the rings, A and the metadata came back
  * unchanged, and writes state_<l>.out (and scale_<l>.out) with the pools as
  * the call left them.
+ *
+ * With EMPTY_CALLS > 0 it then also times that many back-to-back calls whose
+ * active list is empty (every entry -1) on the same stream, after as many
+ * untimed ones, with HIP events, and prints "empty_call_us <mean>": the cost
+ * of a call with nothing to do, host side included, with no Python involved.
  *
  * Exit status: 0 done; 1 usage, file or host-check error; 2 a library status
  * other than the one expected; 3 a HIP runtime error; 4 the call changed a
@@ -151,7 +156,9 @@ static int64_t pool_slots(const blob *b, int64_t stride, size_t eb) {
 }
 
 int main(int argc, char **argv) {
-  if (argc != 2) die(1, "usage", "materialize_caller DIR");
+  if (argc != 2 && argc != 3) die(1, "usage", "materialize_caller DIR [EMPTY_CALLS]");
+  const long empty_calls = argc == 3 ? strtol(argv[2], NULL, 10) : 0;
+  if (empty_calls < 0 || empty_calls > 1000000) die(1, "EMPTY_CALLS out of range", argv[2]);
   g_dir = argv[1];
 
   char path[4096];
@@ -300,8 +307,36 @@ int main(int argc, char **argv) {
               : rssm_materialize(&desc, &tab, (void *)stream);
   if (st != RSSM_OK) die(2, ncp > 0 ? "rssm_materialize_checkpoints" : "rssm_materialize", rssm_last_error());
   HIP_OK(hipStreamSynchronize(stream));
-  HIP_OK(hipStreamDestroy(stream));
   printf("materialize ok\n");
+
+  if (empty_calls > 0) {
+    /* the same call with nothing to do: every active entry -1 */
+    int32_t *none = (int32_t *)malloc(B4);
+    if (!none) die(1, "out of host memory", NULL);
+    for (int b = 0; b < B; ++b) none[b] = -1;
+    void *d_none = device_copy(none, B4);
+    rssm_materialize_tables idle = tab;
+    idle.active_request_indices = (const int32_t *)d_none;
+    hipEvent_t e0, e1;
+    HIP_OK(hipEventCreate(&e0));
+    HIP_OK(hipEventCreate(&e1));
+    for (long i = 0; i < empty_calls; ++i)
+      if (rssm_materialize(&desc, &idle, (void *)stream) != RSSM_OK) die(2, "rssm_materialize", rssm_last_error());
+    HIP_OK(hipStreamSynchronize(stream));
+    HIP_OK(hipEventRecord(e0, stream));
+    for (long i = 0; i < empty_calls; ++i)
+      if (rssm_materialize(&desc, &idle, (void *)stream) != RSSM_OK) die(2, "rssm_materialize", rssm_last_error());
+    HIP_OK(hipEventRecord(e1, stream));
+    HIP_OK(hipEventSynchronize(e1));
+    float ms = 0.0f;
+    HIP_OK(hipEventElapsedTime(&ms, e0, e1));
+    printf("empty_call_us %.3f\n", 1000.0 * ms / (double)empty_calls);
+    HIP_OK(hipEventDestroy(e0));
+    HIP_OK(hipEventDestroy(e1));
+    HIP_OK(hipFree(d_none));
+    free(none);
+  }
+  HIP_OK(hipStreamDestroy(stream));
 
   for (int l = 0; l < L; ++l)
     if (!unchanged(&x[l]) || !unchanged(&Bm[l]) || !unchanged(&dt[l]) || !unchanged(&A[l]))

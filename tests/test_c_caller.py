@@ -285,3 +285,20 @@ def test_step_caller_commit_matches_the_oracle(tmp_path, seed, wg):
     got = np.fromfile(tmp_path / "checkpoint_state.out", np.float32).reshape(prob.state.shape)
     w = test_gpu_gdn.check(prob, got, f"C caller gdn_small/{seed}")
     assert w.any()
+
+
+@pytest.mark.gpu
+def test_empty_call_cost_from_c(tmp_path):
+    """A call whose active list is empty, made back to back from C (no
+    Python): the pages' no-write case.  The bf16 64x128 instance at its
+    default grid (the resident capacity), as in the large workloads; the
+    cost must stay within 5 us per call."""
+    prob = ri.make_problem(ri.CONFIGS["mid_bf16"], 1001)
+    write_problem(prob, tmp_path)
+    res = subprocess.run([caller_exe(), str(tmp_path), "2000"], capture_output=True, text=True, timeout=120)
+    say(res.stdout.strip().replace("\n", " | "))
+    assert res.returncode == 0, (res.returncode, res.stdout, res.stderr)
+    us = float(re.search(r"empty_call_us ([0-9.]+)", res.stdout).group(1))
+    grid = int(re.search(r"launch grid=(\d+)", res.stdout).group(1))
+    say("empty call from C:", us, "us per call at grid", grid)
+    assert us <= 5.0, us
