@@ -180,10 +180,10 @@ int main(int argc, char **argv) {
   if (L < 1 || L > MAX_LAYERS || B < 1 || desc.num_heads < 1 || desc.heads_per_group < 1 ||
       desc.num_heads % desc.heads_per_group)
     die(1, "problem sizes out of range in", path);
-  static int64_t strides[5][MAX_LAYERS]; /* state scale x B dt */
+  static long long strides[5][MAX_LAYERS]; /* state scale x B dt */
   for (int l = 0; l < L; ++l)
     for (int k = 0; k < 5; ++k)
-      if (fscanf(pf, "%lld", (long long *)&strides[k][l]) != 1) die(1, "missing strides in", path);
+      if (fscanf(pf, "%lld", &strides[k][l]) != 1) die(1, "missing strides in", path);
   fclose(pf);
 
   static blob state[MAX_LAYERS], scale[MAX_LAYERS], x[MAX_LAYERS], Bm[MAX_LAYERS], dt[MAX_LAYERS],
