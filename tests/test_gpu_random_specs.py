@@ -53,7 +53,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("i", range(64))
+@pytest.mark.parametrize("i", range(256))
 def test_random_spec_matches_oracle(dev, i):
     import test_gpu_parity as tp
     spec = draw(i)
@@ -86,7 +86,7 @@ def draw_checkpoints(i: int):
     return spec, n_ck, opts
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(96))
 def test_random_checkpoint_spec_matches_oracle(dev, i):
     import parity
     import test_gpu_checkpoints as tc
@@ -111,7 +111,7 @@ def draw_gdn(i: int) -> "ri.GdnSpec":
                       track=bool(rng.random() < 0.6), zero_frac=float(rng.choice([0.0, 0.2])))
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(64))
 def test_random_gdn_spec_matches_oracle(dev, i):
     import test_gpu_gdn as tg
     spec = draw_gdn(i)
@@ -141,7 +141,7 @@ def draw_ssu(i: int) -> "ri.SsuSpec":
                       has_bias=bias, dt_softplus=softplus, pad_frac=float(rng.choice([0.0, 0.3])))
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(64))
 def test_random_decode_spec_matches_oracle(dev, i):
     import test_gpu_ssu as ts
     spec = draw_ssu(i)
