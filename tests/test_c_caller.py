@@ -203,6 +203,22 @@ def test_step_caller_refuses_out_of_range_metadata(tmp_path):
     os.remove(tmp_path / "gdn_bad_accept" / "rawk_cache.bin")
     res = run_step("gdn", tmp_path / "gdn_bad_accept", timeout=60)
     assert res.returncode == 1 and "cannot open" in res.stderr, (res.returncode, res.stderr)
+    # a track slot that is another request's live state slot
+    g = ri.make_gdn_problem(ri.GDN_CONFIGS["gdn_small"], 42)
+    live = [b for b in range(g.spec.B) if g.state_indices[b] > g.spec.null_block_id]
+    assert g.track_state_indices is not None and len(live) >= 2
+    g.track_state_indices[live[0]] = g.state_indices[live[1]]
+    (tmp_path / "gdn_bad_track").mkdir()
+    write_gdn(g, tmp_path / "gdn_bad_track")
+    res = run_step("gdn", tmp_path / "gdn_bad_track", timeout=60)
+    assert res.returncode == 1 and "track slot" in res.stderr, (res.returncode, res.stderr)
+    # a decode-step tensor of the wrong size
+    (tmp_path / "ssu_bad_size").mkdir()
+    prob = ri.make_ssu_problem(ri.SSU_CONFIGS["ssu_small"], 43)
+    write_ssu(prob, tmp_path / "ssu_bad_size")
+    np.zeros(3, np.float32).tofile(tmp_path / "ssu_bad_size" / "A.bin")
+    res = run_step("ssu", tmp_path / "ssu_bad_size", timeout=60)
+    assert res.returncode == 1 and "the shapes give" in res.stderr, (res.returncode, res.stderr)
 
 
 # --------------------------------------------------------------------------
